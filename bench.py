@@ -1,0 +1,260 @@
+"""Benchmark of the sparse-attention hot path on one MI355X.
+
+A step is one prefill layer of the 32K-token Llama-3.1-8B-shaped workload
+(32 query / 8 KV heads, d=128, bf16, block 128, keep 10% + sink + 2 local):
+fused RoPE + dual-band pooling + block scores, block top-k, and block-sparse
+attention.  Inputs are generated in HBM before timing.  The JSON line also
+carries the 128K prefill layer and the 64K / 128K decode steps measured in
+the same run ("secondary"), the roofline of the dominant kernel, and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-secondary] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse prefill tok/s @32K/128K; decode µs/step @64K; % MFMA/HBM peak"
+PEAK_BF16_FLOPS = 2.5e15
+PEAK_HBM_BPS = 8.0e12
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_flops(blk_idx, blk_cnt, block, d, causal=True):
+    """Algorithmic FLOPs of the sparse attention: 4*d per unmasked selected
+    (query, key) pair; also the tile FLOPs (diagonal tiles counted whole)."""
+    B, Hq, N, _ = blk_idx.shape
+    pairs = 0
+    tiles = 0
+    for I in range(N):
+        c = blk_cnt[:, :, I]
+        sel = blk_idx[:, :, I, :]
+        valid = (np.arange(sel.shape[-1])[None, None, :] < c[..., None]) & (sel >= 0)
+        below = valid & (sel < I)
+        diag = valid & (sel == I)
+        pairs += int(below.sum()) * block * block + int(diag.sum()) * block * (block + 1) // 2
+        tiles += int((below | diag).sum()) * block * block
+    return 4.0 * d * pairs, 4.0 * d * tiles
+
+
+def decode_bytes(tok_cnt, d, elem=2):
+    """Gathered K and V bytes per call: every selected token of every (b, h)."""
+    return float(tok_cnt.sum()) * 2 * d * elem
+
+
+def time_prefill(layer, steps, warmup, torch):
+    for _ in range(warmup):
+        layer.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record()
+        layer.score()
+        e[1].record()
+        layer.select()
+        e[2].record()
+        layer.attend()
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    return dict(step_ms=float(np.mean(step_ms)), wall_ms=wall * 1e3,
+                score_ms=float(parts[:, 0].mean()), select_ms=float(parts[:, 1].mean()),
+                attend_ms=float(parts[:, 2].mean()), attend_ms_p10=float(np.percentile(parts[:, 2], 10)),
+                attend_ms_p90=float(np.percentile(parts[:, 2], 90)))
+
+
+def time_decode(step, steps, warmup, torch):
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        e = ev[i]
+        e[0].record()
+        step.rope()
+        e[1].record()
+        step.score()
+        e[2].record()
+        step.select()
+        e[3].record()
+        step.attend()
+        e[4].record()
+    torch.cuda.synchronize()
+    parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
+    total = np.array([e[0].elapsed_time(e[4]) for e in ev])
+    return dict(step_us=float(total.mean() * 1e3), rope_us=float(parts[:, 0].mean() * 1e3),
+                score_us=float(parts[:, 1].mean() * 1e3), select_us=float(parts[:, 2].mean() * 1e3),
+                attend_us=float(parts[:, 3].mean() * 1e3))
+
+
+def run_prefill(cfg, steps, warmup, torch):
+    import synth.device as SD
+    from long_context_sparse_apply_amd.pipeline import PrefillLayer
+    q, k, v = SD.prefill_tensors(cfg)
+    layer = PrefillLayer(q, k, v, theta=cfg.theta, block=cfg.block,
+                         band_split_pair=cfg.band_split_pair, n_sink=cfg.n_sink,
+                         n_local=cfg.n_local, keep_const=cfg.keep_const,
+                         keep_percent=cfg.keep_percent)
+    t = time_prefill(layer, steps, warmup, torch)
+    fl, tile_fl = prefill_flops(layer.blk_idx.cpu().numpy(), layer.blk_cnt.cpu().numpy(),
+                                cfg.block, cfg.d)
+    t["attend_tflops"] = fl / (t["attend_ms"] * 1e-3) / 1e12
+    t["attend_mfma_frac"] = fl / (t["attend_ms"] * 1e-3) / PEAK_BF16_FLOPS
+    t["attend_flops"] = fl
+    t["attend_tile_flops"] = tile_fl
+    t["tok_per_s"] = cfg.B * cfg.S / (t["step_ms"] * 1e-3)
+    # fused RoPE + pooling reads Q and K and writes rotated Q and K once
+    rp_bytes = 2.0 * (q.numel() + k.numel()) * q.element_size()
+    t["score_hbm_bytes"] = rp_bytes
+    del layer, q, k, v
+    torch.cuda.empty_cache()
+    return t
+
+
+def run_decode(cfg, steps, warmup, torch):
+    import synth.device as SD
+    from long_context_sparse_apply_amd.pipeline import DecodeStep
+    dt = SD.decode_tensors(cfg)
+    step = DecodeStep(dt["q_raw"], dt["k"], dt["v"], dt["lens"], dt["dom"], theta=cfg.theta,
+                      top_k=cfg.k, slab=bool(cfg.slab), k_rest=dt["k_rest"])
+    t = time_decode(step, steps, warmup, torch)
+    gb = decode_bytes(step.tok_cnt.cpu().numpy(), cfg.d)
+    t["attend_gather_bytes"] = gb
+    t["attend_hbm_frac"] = gb / (t["attend_us"] * 1e-6) / PEAK_HBM_BPS
+    row = 2 * cfg.n_dom if cfg.slab else cfg.d
+    scan = float(cfg.B) * cfg.Hkv * cfg.L * row * 2 + float(cfg.B) * cfg.Hq * cfg.L * 4
+    t["score_bytes"] = scan
+    t["score_hbm_frac"] = scan / (t["score_us"] * 1e-6) / PEAK_HBM_BPS
+    del step, dt
+    torch.cuda.empty_cache()
+    return t
+
+
+def cpu_baseline(cfg):
+    """The fp64 oracle on two KV groups (8 query heads) of the workload,
+    scaled to the whole layer (work is linear in heads)."""
+    from oracle import sparse_attention as O
+    from synth import workloads as W
+    heads = list(range(2 * cfg.group))  # two KV groups
+    q, k, v, _ = W.prefill_inputs_host(cfg, q_heads=heads)
+    t0 = time.perf_counter()
+    O.prefill_pipeline(q, k[:, :2], v[:, :2], theta=cfg.theta, block=cfg.block,
+                       split_pair=cfg.band_split_pair, calibrate=True, sm_scale=cfg.d ** -0.5,
+                       causal=True, budget=O.keep_budget(cfg.N, keep_percent=cfg.keep_percent),
+                       n_sink=cfg.n_sink, n_local=cfg.n_local, q_heads=heads, group=cfg.group)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    scale = cfg.Hq / len(heads)
+    full_s = dt * scale
+    return {"value": cfg.B * cfg.S / full_s, "unit": "tok/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(heads)} of {cfg.Hq} query heads (2 of {cfg.Hkv} KV groups) of the "
+                      f"32K prefill layer: {dt:.1f} s, scaled x{scale:g} (work is linear in heads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default=None, help="C2|C3|C4|C5: run one workload (profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only; this build has no multi-GPU path "
+              "(see the sharding design).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_sparse_apply_amd  # noqa: F401  (fails loudly if not built)
+    from synth import workloads as W
+    torch.cuda.set_device(0)
+
+    if args.only:
+        cfg = W.CONFIGS[args.only]
+        log(f"running {args.only} only")
+        r = run_prefill(cfg, args.steps, args.warmup, torch) if args.only in ("C2", "C3") \
+            else run_decode(cfg, args.steps, args.warmup, torch)
+        log(json.dumps(r))
+        return
+
+    cfg = W.C2
+    log("C2: prefill 32K")
+    main_r = run_prefill(cfg, args.steps, args.warmup, torch)
+    log(json.dumps(main_r))
+    secondary = {}
+    if not args.no_secondary:
+        log("C3: prefill 128K")
+        r3 = run_prefill(W.C3, max(3, args.steps // 4), 2, torch)
+        log(json.dumps(r3))
+        secondary["prefill_128k"] = {"tok_per_s": r3["tok_per_s"], "ms_per_step": r3["step_ms"],
+                                     "attend_ms": r3["attend_ms"],
+                                     "attend_mfma_frac": r3["attend_mfma_frac"],
+                                     "score_ms": r3["score_ms"], "select_ms": r3["select_ms"]}
+        for name, c in (("decode_64k", W.C4), ("decode_128k_slab", W.C5)):
+            log(f"{name}")
+            rd = run_decode(c, args.steps, args.warmup, torch)
+            log(json.dumps(rd))
+            secondary[name] = {"us_per_step": rd["step_us"], "rope_us": rd["rope_us"],
+                               "score_us": rd["score_us"], "select_us": rd["select_us"],
+                               "attend_us": rd["attend_us"],
+                               "attend_hbm_frac": rd["attend_hbm_frac"],
+                               "score_hbm_frac": rd["score_hbm_frac"]}
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(cfg)
+    achieved = main_r["attend_flops"] / (main_r["attend_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": main_r["tok_per_s"],
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped sparse prefill layer, seq 32768, 32 Q / 8 KV "
+                               "heads, d=128, block 128, keep 10% + sink + 2 local, bf16",
+                   "seq_len": cfg.S, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
+                   "head_dim": cfg.d, "block": cfg.block, "keep_percent": cfg.keep_percent},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16_FLOPS,
+                     "traffic": None, "kernel": "prefill_mfma_kernel",
+                     "avg_launch_ms": main_r["attend_ms"],
+                     "flops_per_launch": main_r["attend_flops"],
+                     "tile_flops_per_launch": main_r["attend_tile_flops"]},
+        "stages_ms": {"score": main_r["score_ms"], "select": main_r["select_ms"],
+                      "attend": main_r["attend_ms"]},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * sa.h -- C ABI of the MI355X (gfx950) RoPE-aware sparse-attention library.
+ *
+ * The method (from the web summaries "Prism: Spectral-Aware Block-Sparse
+ * Attention" and "FASA: Frequency-aware Sparse Attention"): a cheap proxy
+ * scores key blocks (prefill) or cached tokens (decode), a per-query top-k
+ * keeps the best ones, and exact full-dimension softmax attention runs only
+ * over the kept keys, at their original positions.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are device memory owned by the caller, contiguous, layout BHSD
+ *    ([batch, head, sequence, head_dim]) unless stated.  The library never
+ *    allocates or frees memory; scratch space is passed in as a workspace
+ *    whose size comes from sa_workspace_bytes().
+ *  - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream);
+ *    no call synchronises the host.  Calls that share a workspace must be
+ *    ordered on one stream.
+ *  - All argument checks run on the host before any launch; a failing check
+ *    returns its status and launches nothing.  A launch error returns
+ *    SA_ERR_HIP.  Nothing is thrown across the ABI.
+ *  - Floating-point tensors are SA_F32 or SA_BF16 (bf16 = upper half of an
+ *    IEEE fp32, round-to-nearest-even on every store).  Scores, pooled
+ *    vectors and log-sum-exp outputs are always fp32.  Index outputs int32.
+ *  - Supported head_dim: 64 or 128.  Rotary pairs are half-split: pair i is
+ *    channels (i, i + d/2), rotated by p * theta^(-2i/d) at position p.
+ *  - Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
+ *  - The library keeps no mutable global state; distinct streams may call it
+ *    concurrently with distinct buffers.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  SA_ERR_SHAPE = 2,       /* sizes inconsistent (S % block, Hq % Hkv, ...)      */
+  SA_ERR_DTYPE = 3,       /* unknown dtype                                      */
+  SA_ERR_RANGE = 4,       /* a parameter outside its documented range           */
+  SA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required         */
+  SA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement        */
+  SA_ERR_HIP = 7          /* a HIP launch or runtime call failed                */
+} sa_status;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* operation ids for sa_workspace_bytes */
+enum { SA_OP_BLOCK_SCORE = 1, SA_OP_TOPK = 2, SA_OP_DECODE = 3 };
+
+/*
+ * sa_rope_apply -- rotary position encoding at absolute positions.
+ * FASA sec. 2.A (RoPE frequency chunks) and sec. 2.B (attention keeps the
+ * tokens' original absolute positions).
+ *   x, out : [B, H, S, d] dtype; out may equal x (in place).
+ *   pos    : device int32 [B * S] (position of token s of batch b at
+ *            pos[b * S + s]), or NULL for position pos0 + s.
+ *   theta  : RoPE base (> 1).
+ * The angle p * omega_i is formed and reduced modulo 2*pi in fp64, the
+ * rotation is applied in fp32, then stored in dtype.
+ * Errors: SA_ERR_NULL (x/out), SA_ERR_SHAPE (B, H, S < 1 or d not 64/128),
+ *         SA_ERR_RANGE (theta <= 1, pos0 < 0), SA_ERR_DTYPE.
+ */
+sa_status sa_rope_apply(const void* x, void* out, sa_dtype dtype, int B, int H, int S, int d,
+                        const int32_t* pos, int pos0, double theta, void* stream);
+
+/*
+ * sa_block_score -- Prism block importance estimation for prefill.
+ * Prism sec. 1 (block importance from mean-pooled block vectors), sec. 3
+ * item 1 (dual-band pooling), sec. 3 item 2 (energy-based temperature
+ * calibration), sec. 5 (block-level matrix products only).
+ *   q : [B, Hq, S, d], k : [B, Hkv, S, d], raw (not yet rotated), dtype.
+ *   Tokens sit at positions 0 .. S-1.  S % block == 0, N = S / block,
+ *   block in {16, 32, 64, 128, 256}.
+ *   band_split_pair: pairs [0, split) form the high-frequency band, pairs
+ *   [split, d/2) the low band; 0 or d/2 gives a single band.
+ *   calibrate: 1 -> per (block, band) the mean m is rescaled by
+ *   e_tok / e_pool (token RMS energy over pooled RMS energy; 0 if e_pool is
+ *   0); 0 -> plain means.
+ *   causal: 1 -> scores[.., I, J] = -inf for J > I.
+ *   q_rope_out / k_rope_out (nullable): rotated Q / K written in dtype, as
+ *   the sparse attention reads them (one pass over Q and K for both).
+ *   pooled_q_out [B, Hq, N, d] / pooled_k_out [B, Hkv, N, d] (nullable):
+ *   calibrated pooled vectors, fp32.
+ *   scores [B, Hq, N, N] fp32:  sm_scale * <pooled_q(h, I), pooled_k(g(h), J)>.
+ *   ws / ws_bytes: workspace for the pooled vectors whose output pointer is
+ *   NULL; sa_workspace_bytes(SA_OP_BLOCK_SCORE, B*(Hq+Hkv)*N, d, 0, 0, 0)
+ *   bytes always suffice (ws may be NULL when both pooled outputs are given).
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_RANGE (split outside [0, d/2],
+ *         theta <= 1), SA_ERR_WORKSPACE, SA_ERR_DTYPE.
+ */
+sa_status sa_block_score(const void* q, const void* k, sa_dtype dtype, int B, int Hq, int Hkv,
+                         int S, int d, double theta, int block, int band_split_pair,
+                         int calibrate, float sm_scale, int causal, void* q_rope_out,
+                         void* k_rope_out, float* pooled_q_out, float* pooled_k_out,
+                         float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sa_token_score -- FASA Token Importance Predictor (sec. 2.B item 1): the
+ * score of each cached token uses only the dominant frequency chunks.
+ *   q_rope : [B, Hq, d] rotated decode queries, dtype.
+ *   slab == 0: k = [B, Hkv, Lmax, d] rotated K cache, k_rest ignored.
+ *   slab == 1: k = k_dom [B, Hkv, Lmax, 2*n_dom] (channel j < n_dom holds
+ *     channel D[j], channel n_dom + j holds D[j] + d/2), k_rest =
+ *     [B, Hkv, Lmax, d - 2*n_dom] (all other channels ascending).  Only
+ *     k_dom is read here (FASA sec. 2.C, computation-optimised variant).
+ *   cache_len : device int32 [B], 1 <= cache_len[b] <= Lmax.
+ *   dom_pairs : device int32 [Hkv, n_dom], ascending distinct pairs < d/2.
+ *   Hq / Hkv must be 1, 2, 4 or 8; with slab == 1, 2*n_dom must be 8, 16,
+ *   32, 64 or 128 (else SA_ERR_UNSUPPORTED).
+ *   scores [B, Hq, Lmax] fp32: sm_scale * sum over i in D of
+ *     (q_i k_i + q_{i+d/2} k_{i+d/2}) for t < cache_len[b]; -inf beyond.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_RANGE (n_dom outside [1, d/2]),
+ *         SA_ERR_DTYPE.  Entries of cache_len / dom_pairs are not checked on
+ *         the host (device data); out-of-range values give undefined output.
+ */
+sa_status sa_token_score(const void* q_rope, const void* k, const void* k_rest, sa_dtype dtype,
+                         int B, int Hq, int Hkv, int Lmax, int d, const int32_t* cache_len,
+                         const int32_t* dom_pairs, int n_dom, int slab, float sm_scale,
+                         float* scores, void* stream);
+
+/*
+ * sa_topk_select -- per-row selection (Prism sec. 1: keep a subset of
+ * relevant blocks; FASA sec. 2.B: the critical token subset T_t).
+ *   scores : [rows, cols] fp32.
+ *   valid_len : device int32 [rows] (0 <= valid_len <= cols), or NULL = cols.
+ *   k_per_row : device int32 [rows], or NULL = k_const for every row.  When
+ *     given, entries are clamped to [0, k_const]; k_const bounds them.
+ *   Per row with n = valid_len: forced = columns [0, n_sink) and the last
+ *   n_local valid columns; from the other valid columns the min(k, count)
+ *   best by (score descending, column ascending) are kept.  NaN ranks as
+ *   -inf, -0 equals +0.  idx_out [rows, max_out] receives forced + kept,
+ *   ascending, padded with -1; count_out [rows] their number.
+ *   max_out >= n_sink + n_local + k_const.
+ *   ws : workspace of sa_workspace_bytes(SA_OP_TOPK, rows, cols, ...) bytes
+ *   (0 today; reserved).
+ * Results are bit-exact and deterministic.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE (rows < 0, cols < 1, cols > 262144),
+ *         SA_ERR_RANGE (k_const, n_sink, n_local < 0; max_out too small).
+ */
+sa_status sa_topk_select(const float* scores, int64_t rows, int cols, const int32_t* valid_len,
+                         const int32_t* k_per_row, int k_const, int n_sink, int n_local,
+                         int32_t* idx_out, int max_out, int32_t* count_out, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * sa_sparse_attn_prefill -- block-sparse softmax attention (Prism sec. 1).
+ *   q_rope [B, Hq, S, d], k_rope [B, Hkv, S, d], v [B, Hkv, S, d], dtype.
+ *   blk_idx [B, Hq, N, max_sel] int32: the key blocks each query block
+ *   attends to (ascending, distinct, < N; entries past blk_cnt ignored);
+ *   blk_cnt [B, Hq, N] int32 in [0, max_sel].
+ *   causal: 1 -> a query at position t sees keys s <= t only (a token mask
+ *   inside the diagonal block; blocks J > I contribute nothing).
+ *   out [B, Hq, S, d] dtype = softmax(sm_scale q k^T) v over the selected
+ *   keys; lse [B, Hq, S] fp32 (nullable) = natural log-sum-exp of the
+ *   scaled logits.  A query with no visible key gets out = 0, lse = -inf.
+ *   bf16 uses bf16 matrix cores with fp32 accumulation and fp32 softmax;
+ *   fp32 computes in fp32 throughout.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE (S % block, block not 64/128 for bf16 or
+ *         not in {16..256}, d), SA_ERR_RANGE (max_sel < 1), SA_ERR_DTYPE.
+ */
+sa_status sa_sparse_attn_prefill(const void* q_rope, const void* k_rope, const void* v,
+                                 sa_dtype dtype, int B, int Hq, int Hkv, int S, int d, int block,
+                                 const int32_t* blk_idx, const int32_t* blk_cnt, int max_sel,
+                                 int causal, float sm_scale, void* out, float* lse, void* stream);
+
+/*
+ * sa_sparse_attn_decode -- FASA Focused Attention Computation (sec. 2.B
+ * item 2): full-dimension attention of one decode query per (b, h) over its
+ * selected tokens, at their original positions (the cache holds rotated keys).
+ *   q_rope [B, Hq, d]; slab == 0: k [B, Hkv, Lmax, d]; slab == 1: k = k_dom
+ *   and k_rest as in sa_token_score (both read; the full key is their
+ *   channel union).  v [B, Hkv, Lmax, d].
+ *   tok_idx [B, Hq, max_k] int32 token positions (< cache_len[b]), tok_cnt
+ *   [B, Hq] in [0, max_k].
+ *   cache_len is accepted for symmetry with sa_token_score and may be NULL:
+ *   the selection already lies inside each cache.  Entries of tok_idx
+ *   outside [0, Lmax) are skipped.  With slab == 1, n_dom must be a
+ *   multiple of 4 (SA_ERR_UNSUPPORTED) and dom_pairs is required.
+ *   out [B, Hq, d] dtype; lse [B, Hq] fp32 (nullable).  Zero tokens ->
+ *   out = 0, lse = -inf.  Split-K partial results (running max, sum, fp32
+ *   accumulators) live in ws and are merged by the log-sum-exp rule.
+ *   ws_bytes >= sa_workspace_bytes(SA_OP_DECODE, 0, 0, B, Hq, max_k).
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_RANGE, SA_ERR_WORKSPACE,
+ *         SA_ERR_DTYPE.
+ */
+sa_status sa_sparse_attn_decode(const void* q_rope, const void* k, const void* k_rest,
+                                const void* v, sa_dtype dtype, int B, int Hq, int Hkv, int Lmax,
+                                int d, const int32_t* cache_len, const int32_t* dom_pairs,
+                                int n_dom, int slab, const int32_t* tok_idx,
+                                const int32_t* tok_cnt, int max_k, float sm_scale, void* out,
+                                float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sa_workspace_bytes -- bytes of workspace an operation needs.
+ *   SA_OP_BLOCK_SCORE: rows = number of pooled vectors B*(Hq+Hkv)*N,
+ *       cols = d -> scratch for the pooled Q and K vectors.
+ *   SA_OP_TOPK: rows, cols -> 0 (reserved).
+ *   SA_OP_DECODE: B, Hq, max_k -> split-K partials (sized for d <= 128).
+ * Returns 0 for an unknown op.
+ */
+size_t sa_workspace_bytes(int op, int64_t rows, int cols, int B, int Hq, int max_k);
+
+/* Human-readable name of a status code (static storage). */
+const char* sa_status_string(sa_status s);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int sa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

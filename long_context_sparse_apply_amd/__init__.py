@@ -1,0 +1,254 @@
+"""Python binding of the MI355X sparse-attention library (libsa_mi355x.so).
+
+Argument marshalling only: every function below takes torch tensors that
+already live on the GPU, checks their dtype/shape/contiguity, and passes raw
+device pointers, sizes and the current HIP stream to the C entry point of the
+same name.  All computation happens in the HIP kernels.  If the shared
+library has not been built, importing this package raises ImportError; there
+is no CPU fallback.
+
+Build: ``python -m long_context_sparse_apply_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsa_mi355x.so")
+
+SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_RANGE, SA_ERR_WORKSPACE, \
+    SA_ERR_UNSUPPORTED, SA_ERR_HIP = range(8)
+SA_F32, SA_BF16 = 0, 1
+SA_OP_BLOCK_SCORE, SA_OP_TOPK, SA_OP_DECODE = 1, 2, 3
+
+EXPORTED = ("sa_rope_apply", "sa_block_score", "sa_token_score", "sa_topk_select",
+            "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_workspace_bytes",
+            "sa_status_string", "sa_version")
+
+
+class SAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m long_context_sparse_apply_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, D, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double,
+                           ctypes.c_float, ctypes.c_size_t)
+    sig = {
+        "sa_rope_apply": [P, P, I, I, I, I, I, P, I, D, P],
+        "sa_block_score": [P, P, I, I, I, I, I, I, D, I, I, I, F, I, P, P, P, P, P, P, SZ, P],
+        "sa_token_score": [P, P, P, I, I, I, I, I, I, P, P, I, I, F, P, P],
+        "sa_topk_select": [P, I64, I, P, P, I, I, I, P, I, P, P, SZ, P],
+        "sa_sparse_attn_prefill": [P, P, P, I, I, I, I, I, I, I, P, P, I, I, F, P, P, P],
+        "sa_sparse_attn_decode": [P, P, P, P, I, I, I, I, I, I, P, P, I, I, P, P, I, F, P, P, P,
+                                  SZ, P],
+        "sa_workspace_bytes": [I, I64, I, I, I, I],
+        "sa_status_string": [I],
+        "sa_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = I
+    lib.sa_workspace_bytes.restype = SZ
+    lib.sa_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def status_string(s: int) -> str:
+    return lib.sa_status_string(int(s)).decode()
+
+
+def workspace_bytes(op: int, rows: int = 0, cols: int = 0, B: int = 0, Hq: int = 0,
+                    max_k: int = 0) -> int:
+    return int(lib.sa_workspace_bytes(op, rows, cols, B, Hq, max_k))
+
+
+# ----------------------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SA_F32
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype=None, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _call(name, *args):
+    st = getattr(lib, name)(*args)
+    if st != SA_OK:
+        raise SAError(name, st)
+
+
+# ----------------------------------------------------------------------------- entry points
+def sa_rope_apply(x, out, theta: float, pos=None, pos0: int = 0, stream=None):
+    """x, out: [B, H, S, d]; pos: int32 [B*S] or None (pos0 + s)."""
+    torch = _torch()
+    _check(x, "x", ndim=4)
+    _check(out, "out", x.dtype, 4)
+    _check(pos, "pos", torch.int32)
+    B, H, S, d = x.shape
+    _call("sa_rope_apply", _ptr(x), _ptr(out), _dtype_code(x), B, H, S, d, _ptr(pos), pos0,
+          float(theta), _stream(stream))
+    return out
+
+
+def sa_block_score(q, k, scores, *, theta: float, block: int, band_split_pair: int,
+                   calibrate: bool = True, sm_scale: float, causal: bool = True, q_rope_out=None,
+                   k_rope_out=None, pooled_q_out=None, pooled_k_out=None, ws=None, stream=None):
+    """q [B,Hq,S,d], k [B,Hkv,S,d] (raw) -> scores [B,Hq,N,N] fp32."""
+    torch = _torch()
+    _check(q, "q", ndim=4)
+    _check(k, "k", q.dtype, 4)
+    _check(scores, "scores", torch.float32, 4)
+    for t, n in ((q_rope_out, "q_rope_out"), (k_rope_out, "k_rope_out")):
+        _check(t, n, q.dtype, 4)
+    for t, n in ((pooled_q_out, "pooled_q_out"), (pooled_k_out, "pooled_k_out"), (ws, "ws")):
+        _check(t, n)
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _call("sa_block_score", _ptr(q), _ptr(k), _dtype_code(q), B, Hq, Hkv, S, d, float(theta),
+          block, band_split_pair, int(bool(calibrate)), float(sm_scale), int(bool(causal)),
+          _ptr(q_rope_out), _ptr(k_rope_out), _ptr(pooled_q_out), _ptr(pooled_k_out),
+          _ptr(scores), _ptr(ws), ws_bytes, _stream(stream))
+    return scores
+
+
+def sa_token_score(q_rope, k, scores, cache_len, dom_pairs, *, sm_scale: float, slab: bool = False,
+                   k_rest=None, d=None, stream=None):
+    """q_rope [B,Hq,d]; k [B,Hkv,Lmax,d] or k_dom [B,Hkv,Lmax,2*n_dom] -> scores [B,Hq,Lmax]."""
+    torch = _torch()
+    _check(q_rope, "q_rope", ndim=3)
+    _check(k, "k", q_rope.dtype, 4)
+    _check(scores, "scores", torch.float32, 3)
+    _check(cache_len, "cache_len", torch.int32, 1)
+    _check(dom_pairs, "dom_pairs", torch.int32, 2)
+    B, Hq, dd = q_rope.shape
+    Hkv, Lmax = k.shape[1], k.shape[2]
+    n_dom = dom_pairs.shape[1]
+    _call("sa_token_score", _ptr(q_rope), _ptr(k), _ptr(k_rest), _dtype_code(q_rope), B, Hq, Hkv,
+          Lmax, dd, _ptr(cache_len), _ptr(dom_pairs), n_dom, int(bool(slab)), float(sm_scale),
+          _ptr(scores), _stream(stream))
+    return scores
+
+
+def sa_topk_select(scores, idx_out, count_out, *, k_const: int, valid_len=None, k_per_row=None,
+                   n_sink: int = 0, n_local: int = 0, ws=None, stream=None):
+    """scores [..., cols] fp32 (rows = product of leading dims) -> idx_out [rows, max_out]."""
+    torch = _torch()
+    _check(scores, "scores", torch.float32)
+    _check(idx_out, "idx_out", torch.int32)
+    _check(count_out, "count_out", torch.int32)
+    _check(valid_len, "valid_len", torch.int32)
+    _check(k_per_row, "k_per_row", torch.int32)
+    cols = scores.shape[-1]
+    rows = scores.numel() // cols
+    max_out = idx_out.shape[-1]
+    if idx_out.numel() != rows * max_out or count_out.numel() != rows:
+        raise ValueError("idx_out / count_out do not match the score rows")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _call("sa_topk_select", _ptr(scores), rows, cols, _ptr(valid_len), _ptr(k_per_row), k_const,
+          n_sink, n_local, _ptr(idx_out), max_out, _ptr(count_out), _ptr(ws), ws_bytes,
+          _stream(stream))
+    return idx_out, count_out
+
+
+def sa_sparse_attn_prefill(q_rope, k_rope, v, blk_idx, blk_cnt, out, *, block: int, sm_scale: float,
+                           causal: bool = True, lse=None, stream=None):
+    """q_rope [B,Hq,S,d], k_rope/v [B,Hkv,S,d], blk_idx [B,Hq,N,max_sel] -> out [B,Hq,S,d]."""
+    torch = _torch()
+    _check(q_rope, "q_rope", ndim=4)
+    _check(k_rope, "k_rope", q_rope.dtype, 4)
+    _check(v, "v", q_rope.dtype, 4)
+    _check(out, "out", q_rope.dtype, 4)
+    _check(blk_idx, "blk_idx", torch.int32, 4)
+    _check(blk_cnt, "blk_cnt", torch.int32, 3)
+    _check(lse, "lse", torch.float32)
+    B, Hq, S, d = q_rope.shape
+    Hkv = k_rope.shape[1]
+    _call("sa_sparse_attn_prefill", _ptr(q_rope), _ptr(k_rope), _ptr(v), _dtype_code(q_rope), B,
+          Hq, Hkv, S, d, block, _ptr(blk_idx), _ptr(blk_cnt), blk_idx.shape[-1],
+          int(bool(causal)), float(sm_scale), _ptr(out), _ptr(lse), _stream(stream))
+    return out
+
+
+def sa_sparse_attn_decode(q_rope, k, v, tok_idx, tok_cnt, out, ws, *, sm_scale: float,
+                          cache_len=None, dom_pairs=None, slab: bool = False, k_rest=None,
+                          lse=None, stream=None):
+    """q_rope [B,Hq,d]; k (or k_dom) / v caches; tok_idx [B,Hq,max_k] -> out [B,Hq,d]."""
+    torch = _torch()
+    _check(q_rope, "q_rope", ndim=3)
+    _check(k, "k", q_rope.dtype, 4)
+    _check(k_rest, "k_rest", q_rope.dtype, 4)
+    _check(v, "v", q_rope.dtype, 4)
+    _check(out, "out", q_rope.dtype, 3)
+    _check(tok_idx, "tok_idx", torch.int32, 3)
+    _check(tok_cnt, "tok_cnt", torch.int32, 2)
+    _check(ws, "ws")
+    _check(lse, "lse", torch.float32)
+    B, Hq, d = q_rope.shape
+    Hkv, Lmax = v.shape[1], v.shape[2]
+    n_dom = 0 if dom_pairs is None else dom_pairs.shape[1]
+    ws_bytes = ws.numel() * ws.element_size()
+    _call("sa_sparse_attn_decode", _ptr(q_rope), _ptr(k), _ptr(k_rest), _ptr(v),
+          _dtype_code(q_rope), B, Hq, Hkv, Lmax, d, _ptr(cache_len), _ptr(dom_pairs), n_dom,
+          int(bool(slab)), _ptr(tok_idx), _ptr(tok_cnt), tok_idx.shape[-1], float(sm_scale),
+          _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
+    return out
+
+
+# ----------------------------------------------------------------------------- setup helpers
+def prefill_row_params(B: int, Hq: int, N: int, *, keep_const: int = 0, keep_percent: int = 0,
+                       causal: bool = True, device="cuda"):
+    """Per-row arguments of sa_topk_select for the B*Hq*N prefill block rows.
+
+    Row (b, h, I) sees I + 1 blocks when causal (all N otherwise) and keeps
+    keep_const blocks, or ceil(keep_percent / 100 * (I + 1)) (exact integer
+    arithmetic).  Returns (valid_len, k_per_row, k_max) with int32 GPU
+    tensors of B*Hq*N entries; built once per shape.
+    """
+    import numpy as np
+    torch = _torch()
+    I = np.arange(N, dtype=np.int64)
+    vis = I + 1 if causal else np.full(N, N, np.int64)
+    kk = np.full(N, keep_const, np.int64) if keep_const else (keep_percent * vis + 99) // 100
+    vl = np.tile(vis, B * Hq).astype(np.int32)
+    kr = np.tile(kk, B * Hq).astype(np.int32)
+    return (torch.from_numpy(vl).to(device), torch.from_numpy(kr).to(device), int(kk.max()))

@@ -1,0 +1,254 @@
+// Focused decode attention over the selected tokens, split-K across CUs.
+//
+// "FASA: Frequency-aware Sparse Attention", sec. 2.B item 2 (full-dimension
+// attention over the selected subset T_t, at the tokens' original positions)
+// and sec. 2.C (both variants read only the selected key/value rows).
+//
+// Grid: (splits, B*Hq).  A work-group takes 256 consecutive entries of one
+// (b, h) selection list; each of its 4 waves takes 64.  A token row (d
+// channels) is spread over LPT = d/8 lanes with one 16-byte load each, so a
+// wave gathers 4 rows per instruction; the wave first loads its 64 indices
+// with one coalesced load and hands them out by shuffle, then issues all its
+// key and value loads before using any (many bytes in flight per lane).
+// Each work-group leaves (max, sum, unnormalised output) for its split in the
+// workspace; a second kernel merges the splits with the log-sum-exp rule
+//     M = max m_s,  L = sum l_s e^{m_s - M},  o = sum o_s e^{m_s - M} / L.
+//
+// With the dominant-slab key layout the key row is the concatenation of its
+// k_dom part (read by the first 2*n_dom/8 lanes) and its k_rest part (the
+// other lanes); the query is permuted to the same channel order, since the
+// dot product does not depend on the order of channels.
+#include "sa_common.hpp"
+
+namespace sa {
+
+constexpr int kDecChunk = 256;
+constexpr int kDecWaves = 4;
+constexpr int kDecPerWave = kDecChunk / kDecWaves;
+
+int decode_splits(int max_k) {
+  const int s = (max_k + kDecChunk - 1) / kDecChunk;
+  return s < 1 ? 1 : s;
+}
+
+size_t decode_ws_bytes(int B, int Hq, int max_k) {
+  const size_t parts = static_cast<size_t>(B) * Hq * decode_splits(max_k);
+  return parts * (2 + 128) * sizeof(float) + 256;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_partial_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ k_rest,
+    const T* __restrict__ v, int Hq, int Hkv, int Lmax, const int32_t* __restrict__ dom,
+    int n_dom, int slab, const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ tok_cnt,
+    int max_k, float scale, int splits, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    float* __restrict__ ws_o) {
+  constexpr int LPT = D / 8;
+  constexpr int TPI = kWave / LPT;
+  constexpr int STEPS = kDecPerWave / TPI;
+  constexpr int P = D / 2;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int sub = lane % LPT;
+  const int grp_tok = lane / LPT;
+  const int split = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int h = bh % Hq;
+  const int b = bh / Hq;
+  const int g = h / (Hq / Hkv);
+  const int cnt = tok_cnt[bh];
+  const int first = split * kDecChunk + wid * kDecPerWave;
+
+  __shared__ int s_ch[D];
+  __shared__ float s_m[kDecWaves], s_l[kDecWaves];
+  __shared__ float s_o[kDecWaves][D];
+
+  // channel order of the key row as read by the lanes
+  const int dom_w = slab ? 2 * n_dom : D;  // channels stored in `k`
+  if (tid == 0) {
+    if (!slab) {
+      for (int c = 0; c < D; ++c) s_ch[c] = c;
+    } else {
+      uint64_t lo = 0, hi = 0;  // dominant channel set, 128 bits
+      for (int j = 0; j < 2 * n_dom; ++j) {
+        const int ch = dom[g * n_dom + (j % n_dom)] + (j >= n_dom ? P : 0);
+        s_ch[j] = ch;
+        if (ch < 64) lo |= 1ull << ch; else hi |= 1ull << (ch - 64);
+      }
+      int r = 2 * n_dom;
+      for (int c = 0; c < D; ++c) {
+        const bool isdom = c < 64 ? ((lo >> c) & 1ull) : ((hi >> (c - 64)) & 1ull);
+        if (!isdom) s_ch[r++] = c;
+      }
+    }
+  }
+  __syncthreads();
+  float qv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    qv[j] = Elem<T>::load1(q + static_cast<int64_t>(bh) * D + s_ch[sub * 8 + j]) * scale;
+
+  const int64_t head_rows = (static_cast<int64_t>(b) * Hkv + g) * Lmax;
+  const T* krow_base;
+  int kstride, kofs;
+  if (!slab || sub * 8 < dom_w) {
+    krow_base = k;
+    kstride = dom_w;
+    kofs = sub * 8;
+  } else {
+    krow_base = k_rest;
+    kstride = D - dom_w;
+    kofs = sub * 8 - dom_w;
+  }
+  const T* vrow_base = v;
+
+  // this wave's 64 indices, one per lane
+  const int my_pos = first + lane;
+  const int my_idx = (my_pos < cnt) ? tok_idx[static_cast<int64_t>(bh) * max_k + my_pos] : -1;
+
+  using Raw = typename Elem<T>::Raw;
+  int tok[STEPS];
+#pragma unroll
+  for (int it = 0; it < STEPS; ++it) {
+    const int t = __shfl(my_idx, it * TPI + grp_tok, kWave);
+    tok[it] = (t >= 0 && t < Lmax) ? t : -1;  // out-of-range entries are ignored
+  }
+
+  // phase 1: gather the key rows (all loads in flight), logits
+  float logit[STEPS];
+  {
+    Raw kr[STEPS];
+#pragma unroll
+    for (int it = 0; it < STEPS; ++it)
+      kr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(krow_base + (head_rows + tok[it]) * kstride + kofs)
+                            : Elem<T>::zero_raw8();
+#pragma unroll
+    for (int it = 0; it < STEPS; ++it) {
+      float kv[8];
+      Elem<T>::unpack8(kr[it], kv);
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a = fmaf(qv[j], kv[j], a);
+#pragma unroll
+      for (int o = LPT / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, kWave);
+      logit[it] = tok[it] >= 0 ? a : -INFINITY;
+    }
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < STEPS; ++it) mloc = fmaxf(mloc, logit[it]);
+  const float mw = wave_max(mloc);
+
+  // phase 2: gather the value rows, weighted sum
+  float lsum = 0.f;
+  float o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = 0.f;
+  if (mw > -INFINITY) {
+    Raw vr[STEPS];
+#pragma unroll
+    for (int it = 0; it < STEPS; ++it)
+      vr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(vrow_base + (head_rows + tok[it]) * D + sub * 8)
+                            : Elem<T>::zero_raw8();
+#pragma unroll
+    for (int it = 0; it < STEPS; ++it) {
+      const float p = tok[it] >= 0 ? __expf(logit[it] - mw) : 0.f;
+      lsum += p;
+      float vv[8];
+      Elem<T>::unpack8(vr[it], vv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = fmaf(p, vv[j], o[j]);
+    }
+  }
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+    lsum += __shfl_xor(lsum, off, kWave);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] += __shfl_xor(o[j], off, kWave);
+  }
+  if (lane == 0) {
+    s_m[wid] = mw;
+    s_l[wid] = lsum;
+  }
+  if (lane < LPT) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_o[wid][lane * 8 + j] = o[j];
+  }
+  __syncthreads();
+  const int64_t part = static_cast<int64_t>(bh) * splits + split;
+  if (tid < D) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w]);
+    float L = 0.f, O = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float f = (s_m[w] > -INFINITY) ? __expf(s_m[w] - M) : 0.f;
+        L += s_l[w] * f;
+        O += s_o[w][tid] * f;
+      }
+    }
+    ws_o[part * D + tid] = O;
+    if (tid == 0) {
+      ws_m[part] = M;
+      ws_l[part] = L;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ ws_m,
+                                                         const float* __restrict__ ws_l,
+                                                         const float* __restrict__ ws_o, int splits,
+                                                         T* __restrict__ out, float* __restrict__ lse) {
+  const int bh = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t base = static_cast<int64_t>(bh) * splits;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_m[base + s]);
+  float L = 0.f, O = 0.f;
+  if (M > -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float m = ws_m[base + s];
+      if (m == -INFINITY) continue;
+      const float f = __expf(m - M);
+      L += ws_l[base + s] * f;
+      O += ws_o[(base + s) * D + t] * f;
+    }
+  }
+  const float res = (L > 0.f) ? O / L : 0.f;
+  Elem<T>::store1(out + static_cast<int64_t>(bh) * D + t, res);
+  if (lse && t == 0) lse[bh] = (L > 0.f) ? M + logf(L) : -INFINITY;
+}
+
+hipError_t launch_decode(const void* q, const void* k, const void* k_rest, const void* v,
+                         int dtype, int B, int Hq, int Hkv, int Lmax, int d,
+                         const int32_t* cache_len, const int32_t* dom, int n_dom, int slab,
+                         const int32_t* tok_idx, const int32_t* tok_cnt, int max_k, float scale,
+                         void* out, float* lse, void* ws, hipStream_t st) {
+  (void)cache_len;
+  const int splits = decode_splits(max_k);
+  const int64_t parts = static_cast<int64_t>(B) * Hq * splits;
+  float* ws_m = static_cast<float*>(ws);
+  float* ws_l = ws_m + parts;
+  float* ws_o = ws_l + parts;
+  const dim3 grid(splits, B * Hq);
+#define SA_DEC(T, D)                                                                              \
+  decode_partial_kernel<T, D><<<grid, 256, 0, st>>>(                                              \
+      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(k_rest),          \
+      static_cast<const T*>(v), Hq, Hkv, Lmax, dom, n_dom, slab, tok_idx, tok_cnt, max_k, scale,  \
+      splits, ws_m, ws_l, ws_o);                                                                  \
+  decode_merge_kernel<T, D><<<dim3(B * Hq), D, 0, st>>>(ws_m, ws_l, ws_o, splits,                 \
+                                                        static_cast<T*>(out), lse)
+  if (dtype == kBF16) {
+    if (d == 128) { SA_DEC(uint16_t, 128); } else { SA_DEC(uint16_t, 64); }
+  } else {
+    if (d == 128) { SA_DEC(float, 128); } else { SA_DEC(float, 64); }
+  }
+#undef SA_DEC
+  return hipGetLastError();
+}
+
+}  // namespace sa

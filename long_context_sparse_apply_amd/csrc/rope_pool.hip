@@ -1,0 +1,258 @@
+// Rotary position encoding, and the fused pass that rotates Q and K and
+// pools them into calibrated dual-band block vectors.
+//
+// "Prism: Spectral-Aware Block-Sparse Attention", sec. 1 (mean-pooled block
+// importance), sec. 3 item 1 (high- and low-frequency bands pooled apart) and
+// sec. 3 item 2 (temperature from the RMS energy density); "FASA:
+// Frequency-aware Sparse Attention", sec. 2.A (RoPE frequency chunks).
+//
+// Data layout: x[B, H, S, d] row-major.  A thread owns 8 consecutive rotary
+// pairs of one token row: channels [8c, 8c+8) and their partners
+// [P+8c, P+8c+8), read as two 16-byte (bf16) or 32-byte (fp32) accesses, so a
+// wave reads whole 256-byte rows with full coalescing.
+#include "sa_common.hpp"
+
+#include <cmath>
+
+namespace sa {
+
+RopeFreq make_rope_freq(int d, double theta) {
+  RopeFreq r{};
+  const int P = d / 2;
+  for (int i = 0; i < P && i < kMaxPairs; ++i)
+    r.f[i] = std::pow(theta, -2.0 * i / d) / (2.0 * M_PI);
+  return r;
+}
+
+// ------------------------------------------------------------------ rotation only
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ x, T* __restrict__ out,
+                                                   int H, int S, const int32_t* __restrict__ pos,
+                                                   int pos0, int64_t rows, RopeFreq fr) {
+  constexpr int P = D / 2;
+  constexpr int CH = P / 8;  // threads per row
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = gid / CH;
+  const int c = static_cast<int>(gid % CH);
+  if (row >= rows) return;
+  const int s = static_cast<int>(row % S);
+  const int64_t b = row / (static_cast<int64_t>(H) * S);
+  const int64_t p = pos ? static_cast<int64_t>(pos[b * S + s]) : static_cast<int64_t>(pos0) + s;
+  const T* src = x + row * D;
+  float a[8], bb[8];
+  Elem<T>::load8(src + 8 * c, a);
+  Elem<T>::load8(src + P + 8 * c, bb);
+  float ra[8], rb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float cs, sn;
+    rot_cos_sin(p, fr.f[8 * c + j], cs, sn);
+    ra[j] = a[j] * cs - bb[j] * sn;
+    rb[j] = bb[j] * cs + a[j] * sn;
+  }
+  T* dst = out + row * D;
+  Elem<T>::store8(dst + 8 * c, ra);
+  Elem<T>::store8(dst + P + 8 * c, rb);
+}
+
+hipError_t launch_rope(const void* x, void* out, int dtype, int B, int H, int S, int d,
+                       const int32_t* pos, int pos0, const RopeFreq& fr, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(B) * H * S;
+  const int CH = d / 16;
+  const int64_t threads = rows * CH;
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (dtype == kBF16) {
+    if (d == 128)
+      rope_kernel<uint16_t, 128><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x),
+                                                       static_cast<uint16_t*>(out), H, S, pos, pos0, rows, fr);
+    else
+      rope_kernel<uint16_t, 64><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x),
+                                                      static_cast<uint16_t*>(out), H, S, pos, pos0, rows, fr);
+  } else {
+    if (d == 128)
+      rope_kernel<float, 128><<<grid, 256, 0, st>>>(static_cast<const float*>(x),
+                                                    static_cast<float*>(out), H, S, pos, pos0, rows, fr);
+    else
+      rope_kernel<float, 64><<<grid, 256, 0, st>>>(static_cast<const float*>(x),
+                                                   static_cast<float*>(out), H, S, pos, pos0, rows, fr);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ rotation + pooling
+// One work-group per (batch b, query block I, KV group g).  It walks the
+// group's head rows -- KV head g, then its Hq/Hkv query heads -- over the
+// block's `block` tokens, so the cos/sin of the block's (position, pair)
+// grid are computed once and kept in registers for all of them.
+//
+// Per head row it rotates every token (fp32), optionally stores the rotated
+// row, sums the rotated channels and the per-band squared norms, then forms
+//   m = sum / block,  e_tok = sqrt(E_band / (block |band|)),
+//   e_pool = sqrt(|m_band|^2 / |band|),  pooled = m * e_tok / e_pool.
+// The sums use the fp32 rotated values before any bf16 rounding.
+template <typename T, int D, int MAXR>
+__global__ __launch_bounds__(256) void rope_pool_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, int Hq, int Hkv, int S, int block,
+    int split, int calibrate, RopeFreq fr, T* __restrict__ q_rope, T* __restrict__ k_rope,
+    float* __restrict__ pq, float* __restrict__ pk) {
+  constexpr int P = D / 2;
+  constexpr int CH = P / 8;         // threads per token row
+  constexpr int RP = 256 / CH;      // rows per pass
+  const int tid = threadIdx.x;
+  const int c = tid % CH;
+  const int r0 = tid / CH;
+  const int N = S / block;
+  const int I = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int grp = Hq / Hkv;
+
+  __shared__ float s_col[RP][D + 1];
+  __shared__ float s_red[2][256 / kWave];
+  __shared__ float s_m[D];
+  __shared__ float s_band[2][2];  // [band][0: energy sum, 1: pooled sq sum]
+  __shared__ float s_fac[2];
+
+  // cos / sin of this thread's (row, pair) grid
+  float cs[MAXR][8], sn[MAXR][8];
+#pragma unroll
+  for (int ri = 0; ri < MAXR; ++ri) {
+    const int r = r0 + ri * RP;
+    const int64_t p = static_cast<int64_t>(I) * block + r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (r < block) rot_cos_sin(p, fr.f[8 * c + j], cs[ri][j], sn[ri][j]);
+      else { cs[ri][j] = 1.f; sn[ri][j] = 0.f; }
+    }
+  }
+
+  for (int hr = 0; hr <= grp; ++hr) {
+    const bool is_k = (hr == 0);
+    const int h = is_k ? g : g * grp + (hr - 1);
+    const int H = is_k ? Hkv : Hq;
+    const T* src = (is_k ? k : q) + ((static_cast<int64_t>(b) * H + h) * S + static_cast<int64_t>(I) * block) * D;
+    T* dst = is_k ? k_rope : q_rope;
+    if (dst) dst += ((static_cast<int64_t>(b) * H + h) * S + static_cast<int64_t>(I) * block) * D;
+    float* pool_out = (is_k ? pk : pq) + ((static_cast<int64_t>(b) * H + h) * N + I) * D;
+
+    float col[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) col[j] = 0.f;
+    float e_hi = 0.f, e_lo = 0.f;
+#pragma unroll
+    for (int ri = 0; ri < MAXR; ++ri) {
+      const int r = r0 + ri * RP;
+      if (r < block) {
+        float a[8], bb[8], ra[8], rb[8];
+        Elem<T>::load8(src + static_cast<int64_t>(r) * D + 8 * c, a);
+        Elem<T>::load8(src + static_cast<int64_t>(r) * D + P + 8 * c, bb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          ra[j] = a[j] * cs[ri][j] - bb[j] * sn[ri][j];
+          rb[j] = bb[j] * cs[ri][j] + a[j] * sn[ri][j];
+          col[j] += ra[j];
+          col[8 + j] += rb[j];
+          const float e = ra[j] * ra[j] + rb[j] * rb[j];
+          if (8 * c + j < split) e_hi += e; else e_lo += e;
+        }
+        if (dst) {
+          Elem<T>::store8(dst + static_cast<int64_t>(r) * D + 8 * c, ra);
+          Elem<T>::store8(dst + static_cast<int64_t>(r) * D + P + 8 * c, rb);
+        }
+      }
+    }
+    // column sums over the RP row groups
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      s_col[r0][8 * c + j] = col[j];
+      s_col[r0][P + 8 * c + j] = col[8 + j];
+    }
+    e_hi = wave_sum(e_hi);
+    e_lo = wave_sum(e_lo);
+    if ((tid & (kWave - 1)) == 0) {
+      s_red[0][tid / kWave] = e_hi;
+      s_red[1][tid / kWave] = e_lo;
+    }
+    __syncthreads();
+    if (tid < D) {
+      float sum = 0.f;
+      for (int r = 0; r < RP; ++r) sum += s_col[r][tid];
+      s_m[tid] = sum / static_cast<float>(block);
+    }
+    if (tid < 2) {
+      float e = 0.f;
+      for (int w = 0; w < 256 / kWave; ++w) e += s_red[tid][w];
+      s_band[tid][0] = e;
+    }
+    __syncthreads();
+    // pooled squared norms per band
+    {
+      float v = 0.f;
+      int band = 0;
+      if (tid < D) {
+        const int pair = tid % P;
+        band = pair < split ? 0 : 1;
+        v = s_m[tid] * s_m[tid];
+      }
+      float hi = (tid < D && band == 0) ? v : 0.f;
+      float lo = (tid < D && band == 1) ? v : 0.f;
+      hi = wave_sum(hi);
+      lo = wave_sum(lo);
+      if ((tid & (kWave - 1)) == 0) {
+        s_red[0][tid / kWave] = hi;
+        s_red[1][tid / kWave] = lo;
+      }
+    }
+    __syncthreads();
+    if (tid < 2) {
+      float m2 = 0.f;
+      for (int w = 0; w < 256 / kWave; ++w) m2 += s_red[tid][w];
+      const int nch = 2 * (tid == 0 ? split : P - split);
+      float fac = 1.f;
+      if (calibrate) {
+        if (nch == 0 || m2 <= 0.f) {
+          fac = 0.f;
+        } else {
+          const float e_tok = sqrtf(s_band[tid][0] / (static_cast<float>(block) * nch));
+          const float e_pool = sqrtf(m2 / nch);
+          fac = e_tok / e_pool;
+        }
+      }
+      s_fac[tid] = fac;
+    }
+    __syncthreads();
+    if (tid < D) {
+      const int pair = tid % P;
+      pool_out[tid] = s_m[tid] * s_fac[pair < split ? 0 : 1];
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_rope_pool(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int S,
+                            int d, int block, int split, int calibrate, const RopeFreq& fr,
+                            void* q_rope, void* k_rope, float* pq, float* pk, hipStream_t st) {
+  const dim3 grid(S / block, Hkv, B);
+  const int CH = d / 16;
+  const int RP = 256 / CH;
+  const int rows_per_thread = (block + RP - 1) / RP;
+#define SA_RP_LAUNCH(T, D, R)                                                                     \
+  rope_pool_kernel<T, D, R><<<grid, 256, 0, st>>>(                                                \
+      static_cast<const T*>(q), static_cast<const T*>(k), Hq, Hkv, S, block, split, calibrate, fr, \
+      static_cast<T*>(q_rope), static_cast<T*>(k_rope), pq, pk)
+#define SA_RP_R(T, D)                               \
+  if (rows_per_thread <= 1) SA_RP_LAUNCH(T, D, 1);  \
+  else if (rows_per_thread <= 2) SA_RP_LAUNCH(T, D, 2); \
+  else if (rows_per_thread <= 4) SA_RP_LAUNCH(T, D, 4); \
+  else SA_RP_LAUNCH(T, D, 8);
+  if (dtype == kBF16) {
+    if (d == 128) { SA_RP_R(uint16_t, 128) } else { SA_RP_R(uint16_t, 64) }
+  } else {
+    if (d == 128) { SA_RP_R(float, 128) } else { SA_RP_R(float, 64) }
+  }
+#undef SA_RP_R
+#undef SA_RP_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace sa

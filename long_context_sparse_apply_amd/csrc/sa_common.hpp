@@ -1,0 +1,110 @@
+// Device-side helpers shared by the kernels of the sparse-attention library.
+// gfx950 only: wave64, bf16 stored as the upper 16 bits of an IEEE fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa_internal.hpp"
+
+namespace sa {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round to nearest, ties to even; NaN -> quiet NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// two bf16 packed in a uint32 (element 0 in the low half)
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// load / store 8 consecutive elements as fp32 (bf16: one 16-byte access; fp32: two)
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  struct Raw { float4 a, b; };
+  static __device__ __forceinline__ Raw load_raw8(const float* p) {
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+  }
+  static __device__ __forceinline__ Raw zero_raw8() {
+    return Raw{make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  }
+  static __device__ __forceinline__ void unpack8(const Raw& r, float* v) {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+  }
+  static __device__ __forceinline__ void load8(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ void store8(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  static __device__ __forceinline__ float load1(const float* p) { return *p; }
+  static __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+  using Raw = uint4;
+  static __device__ __forceinline__ Raw load_raw8(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+  static __device__ __forceinline__ Raw zero_raw8() { return make_uint4(0u, 0u, 0u, 0u); }
+  static __device__ __forceinline__ void unpack8(const Raw& a, float* v) {
+    v[0] = lo_bf16(a.x); v[1] = hi_bf16(a.x); v[2] = lo_bf16(a.y); v[3] = hi_bf16(a.y);
+    v[4] = lo_bf16(a.z); v[5] = hi_bf16(a.z); v[6] = lo_bf16(a.w); v[7] = hi_bf16(a.w);
+  }
+  static __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    v[0] = lo_bf16(a.x); v[1] = hi_bf16(a.x); v[2] = lo_bf16(a.y); v[3] = hi_bf16(a.y);
+    v[4] = lo_bf16(a.z); v[5] = hi_bf16(a.z); v[6] = lo_bf16(a.w); v[7] = hi_bf16(a.w);
+  }
+  static __device__ __forceinline__ void store8(uint16_t* p, const float* v) {
+    uint4 a;
+    a.x = pack_bf16(v[0], v[1]); a.y = pack_bf16(v[2], v[3]);
+    a.z = pack_bf16(v[4], v[5]); a.w = pack_bf16(v[6], v[7]);
+    *reinterpret_cast<uint4*>(p) = a;
+  }
+  static __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store1(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------- rotary angle
+// cos / sin of 2*pi*frac(p * f) where f = omega / (2*pi) is given in fp64.
+// The product and the reduction to one revolution are exact to ~1e-16
+// revolutions for |p| < 2^31; the remaining angle (|a| <= pi) is evaluated in
+// fp32.
+__device__ __forceinline__ void rot_cos_sin(int64_t p, double f, float& c, float& s) {
+  const double rev = static_cast<double>(p) * f;
+  const double frac = rev - rint(rev);
+  const float ang = static_cast<float>(frac * 6.283185307179586476925286766559);
+  sincosf(ang, &s, &c);
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+}  // namespace sa

@@ -1,0 +1,57 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Every launcher enqueues on `stream` and returns the launch status; all
+// argument checks have already been made by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kMaxPairs = 64;  // head_dim <= 128
+
+// Rotation frequencies in revolutions per position: f_i = theta^(-2i/d) / (2 pi),
+// fp64, computed on the host and passed by value as a kernel argument.
+struct RopeFreq {
+  double f[kMaxPairs];
+};
+RopeFreq make_rope_freq(int d, double theta);
+
+// dtype codes match sa_dtype
+enum { kF32 = 0, kBF16 = 1 };
+
+hipError_t launch_rope(const void* x, void* out, int dtype, int B, int H, int S, int d,
+                       const int32_t* pos, int pos0, const RopeFreq& fr, hipStream_t st);
+
+// fused rotation + calibrated dual-band block pooling of Q and K (one pass)
+hipError_t launch_rope_pool(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int S,
+                            int d, int block, int split, int calibrate, const RopeFreq& fr,
+                            void* q_rope, void* k_rope, float* pq, float* pk, hipStream_t st);
+
+hipError_t launch_block_gemm(const float* pq, const float* pk, int B, int Hq, int Hkv, int N,
+                             int d, float scale, int causal, float* scores, hipStream_t st);
+
+hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_t* valid_len,
+                       const int32_t* k_per_row, int k_const, int n_sink, int n_local,
+                       int32_t* idx_out, int max_out, int32_t* count_out, hipStream_t st);
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                          int Hkv, int S, int d, int block, const int32_t* blk_idx,
+                          const int32_t* blk_cnt, int max_sel, int causal, float scale,
+                          void* out, float* lse, hipStream_t st);
+
+hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
+                              int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
+                              int n_dom, int slab, float scale, float* scores, hipStream_t st);
+
+// decode: split-K partials in ws, then the merge
+int decode_splits(int max_k);
+size_t decode_ws_bytes(int B, int Hq, int max_k);
+hipError_t launch_decode(const void* q, const void* k, const void* k_rest, const void* v,
+                         int dtype, int B, int Hq, int Hkv, int Lmax, int d,
+                         const int32_t* cache_len, const int32_t* dom, int n_dom, int slab,
+                         const int32_t* tok_idx, const int32_t* tok_cnt, int max_k, float scale,
+                         void* out, float* lse, void* ws, hipStream_t st);
+
+}  // namespace sa

@@ -1,0 +1,130 @@
+"""One prefill layer and one decode step as chains of C-ABI calls.
+
+Buffers are allocated once per shape (torch is the allocator); ``run()``
+only enqueues the library's kernels on the current stream.
+
+Prefill ("Prism: Spectral-Aware Block-Sparse Attention"):
+    sa_block_score  -> rotated Q/K, calibrated dual-band pooled vectors, block scores
+    sa_topk_select  -> per query block: sink + local + top-k blocks
+    sa_sparse_attn_prefill -> attention over the selected blocks
+Decode ("FASA: Frequency-aware Sparse Attention"):
+    sa_rope_apply   -> the decode query rotated at position L_b - 1
+    sa_token_score  -> dominant-chunk token scores
+    sa_topk_select  -> top-k tokens
+    sa_sparse_attn_decode -> split-K attention over the selected tokens
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (SA_OP_BLOCK_SCORE, SA_OP_DECODE, prefill_row_params, sa_block_score,
+               sa_rope_apply, sa_sparse_attn_decode, sa_sparse_attn_prefill, sa_token_score,
+               sa_topk_select, workspace_bytes)
+
+
+class PrefillLayer:
+    def __init__(self, q, k, v, *, theta, block, band_split_pair, n_sink, n_local, keep_const=0,
+                 keep_percent=0, calibrate=True, causal=True, sm_scale=None, keep_pooled=False):
+        self.q, self.k, self.v = q, k, v
+        B, Hq, S, d = q.shape
+        Hkv = k.shape[1]
+        self.B, self.Hq, self.Hkv, self.S, self.d = B, Hq, Hkv, S, d
+        self.block, self.N = block, S // block
+        self.theta, self.split = theta, band_split_pair
+        self.calibrate, self.causal = calibrate, causal
+        self.n_sink, self.n_local = n_sink, n_local
+        self.scale = sm_scale if sm_scale is not None else d ** -0.5
+        dev = q.device
+        N = self.N
+        self.q_rope = torch.empty_like(q)
+        self.k_rope = torch.empty_like(k)
+        self.scores = torch.empty((B, Hq, N, N), dtype=torch.float32, device=dev)
+        if keep_pooled:
+            self.pq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+            self.pk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
+            self.ws = None
+        else:
+            self.pq = self.pk = None
+            self.ws = torch.empty(workspace_bytes(SA_OP_BLOCK_SCORE, B * (Hq + Hkv) * N, d),
+                                  dtype=torch.uint8, device=dev)
+        self.valid_len, self.k_rows, kmax = prefill_row_params(
+            B, Hq, N, keep_const=keep_const, keep_percent=keep_percent, causal=causal, device=dev)
+        self.k_max = kmax
+        self.max_sel = min(N, n_sink + n_local + kmax)
+        self.max_out = n_sink + n_local + kmax
+        self.blk_idx = torch.empty((B, Hq, N, self.max_out), dtype=torch.int32, device=dev)
+        self.blk_cnt = torch.empty((B, Hq, N), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+
+    def score(self):
+        sa_block_score(self.q, self.k, self.scores, theta=self.theta, block=self.block,
+                       band_split_pair=self.split, calibrate=self.calibrate, sm_scale=self.scale,
+                       causal=self.causal, q_rope_out=self.q_rope, k_rope_out=self.k_rope,
+                       pooled_q_out=self.pq, pooled_k_out=self.pk, ws=self.ws)
+
+    def select(self):
+        sa_topk_select(self.scores, self.blk_idx, self.blk_cnt, k_const=self.k_max,
+                       valid_len=self.valid_len, k_per_row=self.k_rows, n_sink=self.n_sink,
+                       n_local=self.n_local)
+
+    def attend(self):
+        sa_sparse_attn_prefill(self.q_rope, self.k_rope, self.v, self.blk_idx, self.blk_cnt,
+                               self.out, block=self.block, sm_scale=self.scale, causal=self.causal,
+                               lse=self.lse)
+
+    def run(self):
+        self.score()
+        self.select()
+        self.attend()
+        return self.out
+
+
+class DecodeStep:
+    def __init__(self, q_raw, k, v, cache_len, dom_pairs, *, theta, top_k, slab=False, k_rest=None,
+                 sm_scale=None, cache_len_host=None):
+        self.q_raw, self.k, self.v, self.k_rest = q_raw, k, v, k_rest
+        B, Hq, d = q_raw.shape
+        Hkv, L = v.shape[1], v.shape[2]
+        self.B, self.Hq, self.Hkv, self.L, self.d = B, Hq, Hkv, L, d
+        self.theta, self.top_k, self.slab = theta, top_k, slab
+        self.cache_len, self.dom = cache_len, dom_pairs
+        self.scale = sm_scale if sm_scale is not None else d ** -0.5
+        dev = q_raw.device
+        # position of the decoding token per batch row: cache_len - 1 (int32, [B])
+        self.pos = (cache_len - 1).to(torch.int32).contiguous()
+        self.q_rope = torch.empty_like(q_raw)
+        self.scores = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        self.valid_len = cache_len.repeat_interleave(Hq).to(torch.int32).contiguous()
+        self.tok_idx = torch.empty((B, Hq, top_k), dtype=torch.int32, device=dev)
+        self.tok_cnt = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+        self.ws = torch.empty(workspace_bytes(SA_OP_DECODE, B=B, Hq=Hq, max_k=top_k),
+                              dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(q_raw)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+
+    def rope(self):
+        # q_raw viewed as [B, Hq, 1, d]: one token per (b, h) at position pos[b]
+        sa_rope_apply(self.q_raw.view(self.B, self.Hq, 1, self.d),
+                      self.q_rope.view(self.B, self.Hq, 1, self.d), self.theta, pos=self.pos)
+
+    def score(self):
+        sa_token_score(self.q_rope, self.k, self.scores, self.cache_len, self.dom,
+                       sm_scale=self.scale, slab=self.slab, k_rest=self.k_rest)
+
+    def select(self):
+        sa_topk_select(self.scores, self.tok_idx, self.tok_cnt, k_const=self.top_k,
+                       valid_len=self.valid_len)
+
+    def attend(self):
+        sa_sparse_attn_decode(self.q_rope, self.k, self.v, self.tok_idx, self.tok_cnt, self.out,
+                              self.ws, sm_scale=self.scale, cache_len=self.cache_len,
+                              dom_pairs=self.dom, slab=self.slab, k_rest=self.k_rest,
+                              lse=self.lse)
+
+    def run(self):
+        self.rope()
+        self.score()
+        self.select()
+        self.attend()
+        return self.out

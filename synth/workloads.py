@@ -306,26 +306,31 @@ def decode_needles(cfg: DecodeConfig, lens: np.ndarray) -> list[tuple[int, int, 
     return out
 
 
-def decode_inputs_host(cfg: DecodeConfig, batches=None):
+def decode_inputs_host(cfg: DecodeConfig, batches=None, kv_heads=None):
     """Stored decode inputs on the host for batch rows ``batches``.
 
     Returns dict with q_raw[nb, Hq, d], k[nb, Hkv, L, d] (standard layout,
     already rotated), v[nb, Hkv, L, d], lens[nb], dom[Hkv, n_dom], batches.
+    With ``kv_heads`` only those KV heads' caches are generated (the others
+    stay zero), for sampled checks of large workloads.
     """
     if batches is None:
         batches = list(range(cfg.B))
+    if kv_heads is None:
+        kv_heads = list(range(cfg.Hkv))
     lens_all = cache_lengths(cfg)
     nb = len(batches)
     q = np.empty((nb, cfg.Hq, cfg.d), np.float32)
-    k = np.empty((nb, cfg.Hkv, cfg.L, cfg.d), np.float32)
-    v = np.empty_like(k)
+    k = np.zeros((nb, cfg.Hkv, cfg.L, cfg.d), np.float32)
+    v = np.zeros_like(k)
     for i, b in enumerate(batches):
         q[i] = gaussian_tensor(cfg.seed, TID_Q, (cfg.Hq, cfg.d), cfg.dtype, b * cfg.Hq * cfg.d)
-        base = b * cfg.Hkv * cfg.L * cfg.d
-        k[i] = gaussian_tensor(cfg.seed, TID_K, (cfg.Hkv, cfg.L, cfg.d), cfg.dtype, base)
-        v[i] = gaussian_tensor(cfg.seed, TID_V, (cfg.Hkv, cfg.L, cfg.d), cfg.dtype, base)
+        for g in kv_heads:
+            base = (b * cfg.Hkv + g) * cfg.L * cfg.d
+            k[i, g] = gaussian_tensor(cfg.seed, TID_K, (cfg.L, cfg.d), cfg.dtype, base)
+            v[i, g] = gaussian_tensor(cfg.seed, TID_V, (cfg.L, cfg.d), cfg.dtype, base)
     for b, h, p, row in decode_patches(cfg, lens_all):
-        if b in batches:
+        if b in batches and h // cfg.group in kv_heads:
             k[batches.index(b), h // cfg.group, p] = row
     return dict(q_raw=q, k=k, v=v, lens=lens_all[batches], dom=dominant_pairs(cfg),
                 batches=batches)

@@ -1,0 +1,94 @@
+"""Comparison rules used by the GPU parity tests.
+
+* Scores (fp32 on the GPU, fp64 in the oracle): |gpu - ref| <= 1e-4 *
+  max(|ref|, rms of the row's finite refs); -inf entries must match exactly.
+* Selected index sets: where the oracle's k-th and (k+1)-th candidate scores
+  differ by more than 1e-3 relative (same floor), the sets must be equal;
+  everywhere the GPU's set must be threshold-consistent with the oracle's
+  scores: the worst kept candidate is not clearly worse than the best dropped
+  one (each side widened by the score tolerance), and the count is right.
+* Attention outputs: within 2e-2 absolute for bf16 storage, 1e-5 for fp32.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+SCORE_RTOL = 1e-4
+GAP_RTOL = 1e-3
+OUT_ATOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def row_floor(ref_row: np.ndarray) -> float:
+    fin = ref_row[np.isfinite(ref_row)]
+    return float(np.sqrt(np.mean(fin ** 2))) if fin.size else 0.0
+
+
+def assert_scores_close(gpu: np.ndarray, ref: np.ndarray, rtol: float = SCORE_RTOL):
+    g = np.asarray(gpu, np.float64).reshape(-1, gpu.shape[-1])
+    r = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    assert g.shape == r.shape
+    inf_r = ~np.isfinite(r)
+    assert np.array_equal(~np.isfinite(g), inf_r), "infinite entries differ"
+    assert np.array_equal(g[inf_r], r[inf_r])
+    worst = 0.0
+    for i in range(r.shape[0]):
+        fin = np.isfinite(r[i])
+        if not fin.any():
+            continue
+        tol = rtol * np.maximum(np.abs(r[i][fin]), row_floor(r[i]))
+        err = np.abs(g[i][fin] - r[i][fin])
+        worst = max(worst, float((err / tol).max()))
+        assert np.all(err <= tol), f"row {i}: max err {err.max():.3e} > tol"
+    return worst
+
+
+def candidates(valid_len: int, n_sink: int, n_local: int) -> np.ndarray:
+    forced = set(range(min(n_sink, valid_len))) | set(range(max(0, valid_len - n_local), valid_len))
+    return np.array([j for j in range(valid_len) if j not in forced], dtype=np.int64), forced
+
+
+def check_selection(gpu_sel, ref_scores, valid_len, k, n_sink, n_local, rtol=SCORE_RTOL,
+                    tol=None):
+    """Validate one row's GPU selection against the oracle's scores.
+
+    ``tol`` (optional, per column) replaces the relative score tolerance
+    when the GPU scores carry a larger derived error bound.  Returns True if
+    the gap rule applied (and so the sets were compared for equality), False
+    if only threshold consistency could be checked.
+    """
+    gsel = np.asarray(gpu_sel, dtype=np.int64)
+    assert np.all(np.diff(gsel) > 0), "selection not strictly ascending"
+    cand, forced = candidates(int(valid_len), n_sink, n_local)
+    assert forced <= set(gsel.tolist()), "forced column missing"
+    kk = min(int(k), cand.size)
+    chosen = np.array(sorted(set(gsel.tolist()) - forced), dtype=np.int64)
+    assert chosen.size == kk, f"kept {chosen.size} candidates, expected {kk}"
+    assert np.all(np.isin(chosen, cand))
+    if kk == 0 or kk == cand.size:
+        return True
+    s = np.asarray(ref_scores, np.float64)[cand]
+    s = np.where(np.isnan(s), -np.inf, s)
+    floor = row_floor(s)
+    if tol is None:
+        t = np.where(np.isfinite(s), rtol * np.maximum(np.abs(s), floor), 0.0)
+    else:
+        t = np.where(np.isfinite(s), np.asarray(tol, np.float64)[cand], 0.0)
+    order = np.lexsort((cand, -s))
+    kth, nxt = s[order[kk - 1]], s[order[kk]]
+    gap_need = max(GAP_RTOL * max(abs(kth), floor), 2.0 * (t[order[kk - 1]] + t[order[kk]]))
+    gap_applies = np.isfinite(kth) and (kth - nxt) > gap_need
+    if gap_applies:
+        assert np.array_equal(np.sort(cand[order[:kk]]), chosen), "selection differs despite a clear gap"
+        return True
+    is_kept = np.isin(cand, chosen)
+    worst_kept = np.min((s + t)[is_kept])
+    best_dropped = np.max((s - t)[~is_kept])
+    assert worst_kept >= best_dropped, "selection not threshold-consistent"
+    return False

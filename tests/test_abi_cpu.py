@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "sa.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^\s*(?:sa_status|size_t|const char\*|int)\s+(sa_\w+)\(", src, re.M)))
+
+
+def test_header_declares_the_six_entry_points():
+    names = _declared()
+    for n in ("sa_rope_apply", "sa_block_score", "sa_token_score", "sa_topk_select",
+              "sa_sparse_attn_prefill", "sa_sparse_attn_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import long_context_sparse_apply_amd as sa
+    lib = ctypes.CDLL(sa.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) <= set(sa.EXPORTED)
+
+
+def test_status_strings_and_version():
+    import long_context_sparse_apply_amd as sa
+    assert sa.status_string(0) == "ok"
+    assert "workspace" in sa.status_string(sa.SA_ERR_WORKSPACE)
+    assert sa.lib.sa_version() >= 100
+
+
+def _fake(n=1):
+    # non-NULL host addresses: only reached if validation wrongly passed, never dereferenced
+    return ctypes.c_void_p(0x1000 * n)
+
+
+def test_validation_errors_before_launch():
+    import long_context_sparse_apply_amd as sa
+    L = sa.lib
+    P = _fake
+    # rope: null, bad d, bad theta, bad dtype
+    assert L.sa_rope_apply(None, P(), 1, 1, 1, 8, 128, None, 0, 1e4, None) == sa.SA_ERR_NULL
+    assert L.sa_rope_apply(P(), P(), 1, 1, 1, 8, 96, None, 0, 1e4, None) == sa.SA_ERR_SHAPE
+    assert L.sa_rope_apply(P(), P(), 1, 1, 1, 8, 128, None, 0, 1.0, None) == sa.SA_ERR_RANGE
+    assert L.sa_rope_apply(P(), P(), 7, 1, 1, 8, 128, None, 0, 1e4, None) == sa.SA_ERR_DTYPE
+    # block score: S % block, Hq % Hkv, split range, workspace
+    args = dict(theta=1e4, block=64, split=16)
+    def bs(B=1, Hq=4, Hkv=2, S=512, d=64, block=64, split=16, ws=None, wsb=0, pq=None, pk=None):
+        return L.sa_block_score(P(), P(), 0, B, Hq, Hkv, S, d, 1e4, block, split, 1, 0.1, 1,
+                                None, None, pq, pk, P(), ws, wsb, None)
+    assert bs(S=500) == sa.SA_ERR_SHAPE
+    assert bs(Hq=3) == sa.SA_ERR_SHAPE
+    assert bs(block=48) == sa.SA_ERR_SHAPE
+    assert bs(split=33) == sa.SA_ERR_RANGE
+    assert bs() == sa.SA_ERR_WORKSPACE
+    assert bs(ws=P(), wsb=100) == sa.SA_ERR_WORKSPACE
+    # topk: shapes, ranges, max_out
+    assert L.sa_topk_select(P(), 4, 0, None, None, 2, 0, 0, P(), 4, P(), None, 0, None) == sa.SA_ERR_SHAPE
+    assert L.sa_topk_select(P(), 4, 300000, None, None, 2, 0, 0, P(), 4, P(), None, 0, None) == sa.SA_ERR_SHAPE
+    assert L.sa_topk_select(P(), 4, 10, None, None, -1, 0, 0, P(), 4, P(), None, 0, None) == sa.SA_ERR_RANGE
+    assert L.sa_topk_select(P(), 4, 10, None, None, 4, 1, 1, P(), 5, P(), None, 0, None) == sa.SA_ERR_RANGE
+    assert L.sa_topk_select(None, 4, 10, None, None, 2, 0, 0, P(), 4, P(), None, 0, None) == sa.SA_ERR_NULL
+    assert L.sa_topk_select(None, 0, 10, None, None, 2, 0, 0, None, 4, None, None, 0, None) == sa.SA_OK
+    # token score: group size, slab width
+    assert L.sa_token_score(P(), P(), None, 1, 1, 6, 2, 64, 128, P(), P(), 16, 0, 0.1, P(), None) == sa.SA_ERR_UNSUPPORTED
+    assert L.sa_token_score(P(), P(), None, 1, 1, 8, 2, 64, 128, P(), P(), 6, 1, 0.1, P(), None) == sa.SA_ERR_UNSUPPORTED
+    assert L.sa_token_score(P(), P(), None, 1, 1, 8, 2, 64, 128, P(), P(), 65, 0, 0.1, P(), None) == sa.SA_ERR_RANGE
+    # prefill attention
+    assert L.sa_sparse_attn_prefill(P(), P(), P(), 1, 1, 4, 2, 1000, 128, 128, P(), P(), 4, 1, 0.1, P(), None, None) == sa.SA_ERR_SHAPE
+    assert L.sa_sparse_attn_prefill(P(), P(), P(), 1, 1, 4, 2, 1024, 128, 128, P(), P(), 0, 1, 0.1, P(), None, None) == sa.SA_ERR_RANGE
+    assert L.sa_sparse_attn_prefill(None, P(), P(), 1, 1, 4, 2, 1024, 128, 128, P(), P(), 4, 1, 0.1, P(), None, None) == sa.SA_ERR_NULL
+    # decode attention: workspace and slab rules
+    need = sa.workspace_bytes(sa.SA_OP_DECODE, B=2, Hq=8, max_k=512)
+    assert need > 2 * 8 * 2 * 128 * 4
+    assert L.sa_sparse_attn_decode(P(), P(), None, P(), 1, 2, 8, 2, 1024, 128, P(), None, 0, 0,
+                                   P(), P(), 512, 0.1, P(), None, P(), need - 1, None) == sa.SA_ERR_WORKSPACE
+    assert L.sa_sparse_attn_decode(P(), P(), None, P(), 1, 2, 8, 2, 1024, 128, P(), P(), 6, 1,
+                                   P(), P(), 512, 0.1, P(), None, P(), need, None) == sa.SA_ERR_UNSUPPORTED
+    assert L.sa_sparse_attn_decode(P(), P(), None, P(), 1, 2, 8, 2, 1024, 128, P(), P(), 16, 1,
+                                   P(), P(), 512, 0.1, P(), None, P(), need, None) == sa.SA_ERR_NULL
+
+
+def test_workspace_sizes():
+    import long_context_sparse_apply_amd as sa
+    assert sa.workspace_bytes(sa.SA_OP_TOPK, 100, 1000) == 0
+    n = 1 * (32 + 8) * 256
+    assert sa.workspace_bytes(sa.SA_OP_BLOCK_SCORE, n, 128) >= n * 128 * 4
+    assert sa.workspace_bytes(99) == 0
+
+
+def test_prefill_row_params_budget():
+    import long_context_sparse_apply_amd as sa
+    vl, kr, kmax = sa.prefill_row_params(1, 2, 256, keep_percent=10, device="cpu")
+    assert vl.shape[0] == 512 and int(vl[0]) == 1 and int(vl[255]) == 256 and int(vl[256]) == 1
+    assert int(kr[9]) == 1 and int(kr[10]) == 2 and int(kr[255]) == 26 and kmax == 26
