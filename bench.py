@@ -180,6 +180,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="C2|C3|C4|C5: run one workload (profiling)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first copy 1 GiB device-to-device 3 times (a kernel of known bytes "
+                         "that scales the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only; this build has no multi-GPU path "
@@ -190,6 +193,15 @@ def main():
     from synth import workloads as W
     torch.cuda.set_device(0)
 
+    if args.calib_copy:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 1 GiB x3")
+        del src, dst
+        torch.cuda.empty_cache()
     if args.only:
         cfg = W.CONFIGS[args.only]
         log(f"running {args.only} only")

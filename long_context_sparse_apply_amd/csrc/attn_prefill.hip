@@ -53,37 +53,115 @@ __device__ __forceinline__ void prefill_work_item(int x, int nwg, int B, int Hq,
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
+// LDS tile: BS rows (keys) x D bf16, row-major, rows unpadded; the 16-byte
+// chunk c of row r sits at chunk position c ^ (r % CPR) (XOR swizzle), so the
+// 32 rows one MFMA operand read touches spread over the banks.  Tiles are
+// filled by direct-to-LDS loads (global_load_lds_dwordx4): one wave
+// instruction writes 1 KB of consecutive LDS bytes, lane i its 16 bytes at
+// offset 16 i, and each lane fetches the global chunk that belongs there.
 template <int D, int BS>
-__global__ __launch_bounds__(BS * 2) void prefill_mfma_kernel(
+struct PrefillTile {
+  static constexpr int ROWB = D * 2;                 // bytes per row
+  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  static constexpr int BYTES = BS * ROWB;
+  static constexpr int NW = BS / 32;                 // waves per work-group
+  static constexpr int LPW = BYTES / 1024 / NW;      // load instructions per wave per tile
+
+  static __device__ __forceinline__ int phys(int row, int chunk) {
+    return row * ROWB + ((chunk ^ (row % CPR)) << 4);
+  }
+  // issue this wave's share of the tile's direct-to-LDS loads (asynchronous)
+  static __device__ __forceinline__ void issue(const uint16_t* g, uint8_t* lds, int wid, int lane) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int ins = wid * LPW + j;
+      const int off = ins * 1024 + lane * 16;
+      const int row = off / ROWB;
+      const int pos = (off % ROWB) >> 4;
+      const int chunk = pos ^ (row % CPR);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(g) + row * ROWB + chunk * 16;
+      __builtin_amdgcn_global_load_lds(src, lds + ins * 1024, 16, 0, 0);
+    }
+  }
+};
+
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// One work-group per (b, h, I) with one wave per 32 queries.  Per selected key
+// block J the work-group streams K_J and V_J into LDS asynchronously in a
+// ping-pong: K_{n+1} loads while block n's softmax and P V run, V_{n+1} loads
+// while block n+1's S runs.  Each wave:
+//   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16; A = K from LDS, B = Q^T in registers)
+//   softmax on the accumulators (base 2, scale folded into one FMA); the
+//   running reference max is raised only when a block's max exceeds it by more
+//   than 8 (then O and l are rescaled), so p <= 2^8
+//   O^T += V^T P^T (A = V^T read from the row-major V tile with the LDS
+//   transpose read ds_read_b64_tr_b16; B = P^T straight from the S^T registers)
+template <int D, int BS>
+__global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int B, int Hq, int Hkv, int S, const int32_t* __restrict__ blk_idx,
     const int32_t* __restrict__ blk_cnt, int max_sel, int causal, float scale,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int NT = BS * 2;          // threads: one wave per 32 queries
+  using Tile = PrefillTile<D, BS>;
   constexpr int KS = D / 16;          // k-steps of the QK^T product
   constexpr int KT = BS / 32;         // 32-key tiles per block
   constexpr int DT = D / 32;          // 32-wide d tiles of the output
-  constexpr int KROW = D + 8;         // LDS row pitch of K (bf16), padded
-  constexpr int VROW = BS + 8;        // LDS row pitch of V^T (bf16), padded
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BS * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VROW];
+  constexpr int LPW = Tile::LPW;
+  constexpr float kRescale = 8.f;     // lazy-rescale threshold (base-2 units)
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[Tile::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[Tile::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int grp16 = lane >> 4;
+  const int i16 = lane & 15;
   const int N = S / BS;
   int b, h, I;
   prefill_work_item(blockIdx.x, gridDim.x, B, Hq, Hkv, N, b, h, I);
   const int g = h / (Hq / Hkv);
   const int64_t qrow0 = (static_cast<int64_t>(b) * Hq + h) * S + static_cast<int64_t>(I) * BS;
-  const int64_t kvrow0 = (static_cast<int64_t>(b) * Hkv + g) * S;
+  const uint16_t* kbase = k + (static_cast<int64_t>(b) * Hkv + g) * S * D;
+  const uint16_t* vbase = v + (static_cast<int64_t>(b) * Hkv + g) * S * D;
   const int64_t sel0 = ((static_cast<int64_t>(b) * Hq + h) * N + I);
+
+  // the block list, read with uniform (scalar) loads; entries out of range or
+  // above the diagonal (causal) are skipped
   const int cnt = blk_cnt[sel0];
   const int32_t* sel = blk_idx + sel0 * max_sel;
+  auto next_valid = [&](int from) {
+    for (int t = from; t < cnt; ++t) {
+      const int J = sel[t];
+      if (J >= 0 && J < N && !(causal && J > I)) return t;
+    }
+    return cnt;
+  };
 
-  // Q^T fragments: this lane's query (row wid*32 + l32) and 8 channels per k-step
+  // Q^T fragments: this lane's query and 8 channels per k-step
   const int qloc = wid * 32 + l32;
   bf16x8 qf[KS];
   {
@@ -102,49 +180,23 @@ __global__ __launch_bounds__(BS * 2) void prefill_mfma_kernel(
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
-  float m_run = -INFINITY;  // running max (base-2 units) of this lane's query
-  float l_run = 0.f;
+  float m_ref = -INFINITY;  // reference max (base 2) of this lane's query
+  float l_part = 0.f;       // this lane's half of the softmax denominator
 
-  for (int si = 0; si < cnt; ++si) {
-    const int J = sel[si];
-    if (J < 0 || J >= N || (causal && J > I)) continue;  // uniform across the work-group
-    __syncthreads();  // previous block's LDS reads are done
-    // stage K rows (16-byte chunks) and V transposed (4 keys x 8 channels per chunk)
-    {
-      const uint16_t* kp = k + (kvrow0 + static_cast<int64_t>(J) * BS) * D;
-      constexpr int KCH = BS * D / 8;
-#pragma unroll
-      for (int c = tid; c < KCH; c += NT) {
-        const int row = c / (D / 8), col8 = c % (D / 8);
-        const uint4 w = *reinterpret_cast<const uint4*>(kp + static_cast<int64_t>(row) * D + col8 * 8);
-        *reinterpret_cast<uint4*>(&sK[row * KROW + col8 * 8]) = w;
-      }
-      const uint16_t* vp = v + (kvrow0 + static_cast<int64_t>(J) * BS) * D;
-      constexpr int VCH = (BS / 4) * (D / 8);
-#pragma unroll
-      for (int c = tid; c < VCH; c += NT) {
-        const int col8 = c % (D / 8), kq = c / (D / 8);
-        uint4 w[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          w[r] = *reinterpret_cast<const uint4*>(vp + static_cast<int64_t>(kq * 4 + r) * D + col8 * 8);
-        // element e of row r: channel col8*8 + e, key kq*4 + r
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t vals[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t word = (e < 2) ? w[r].x : (e < 4) ? w[r].y : (e < 6) ? w[r].z : w[r].w;
-            vals[r] = (e & 1) ? (word >> 16) : (word & 0xffffu);
-          }
-          u32x2 pk = {vals[0] | (vals[1] << 16), vals[2] | (vals[3] << 16)};
-          *reinterpret_cast<u32x2*>(&sV[(col8 * 8 + e) * VROW + kq * 4]) = pk;
-        }
-      }
-    }
-    __syncthreads();
+  int t = next_valid(0);
+  if (t < cnt) {
+    Tile::issue(kbase + static_cast<int64_t>(sel[t]) * BS * D, sK, wid, lane);
+    Tile::issue(vbase + static_cast<int64_t>(sel[t]) * BS * D, sV, wid, lane);
+  }
+  while (t < cnt) {
+    const int J = sel[t];
+    const int tn = next_valid(t + 1);
+    const bool more = tn < cnt;
+    const int Jn = more ? sel[tn] : 0;
+    // (A) K_n has landed for every wave
+    wait_vmcnt<LPW>();
+    __builtin_amdgcn_s_barrier();
 
-    // S^T = K Q^T for the block: KT tiles of 32 keys x 32 queries
     f32x16 sacc[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -152,13 +204,19 @@ __global__ __launch_bounds__(BS * 2) void prefill_mfma_kernel(
       for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&sK[(kt * 32 + l32) * KROW + 16 * s + 8 * hi]);
+        const uint4 w = *reinterpret_cast<const uint4*>(&sK[Tile::phys(kt * 32 + l32, 2 * s + hi)]);
         u32x4 t = {w.x, w.y, w.z, w.w};
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, t), qf[s],
                                                             sacc[kt], 0, 0, 0);
       }
     }
-    // scale to base-2 units, causal mask on the diagonal block, block max
+    // (B) every wave is done with sK and V_n has landed: start K_{n+1}
+    wait_lgkm0();
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (more) Tile::issue(kbase + static_cast<int64_t>(Jn) * BS * D, sK, wid, lane);
+
+    // softmax: block max per query (this lane's 16 keys per tile and lane ^ 32)
     const bool diag = causal && (J == I);
     float mblk = -INFINITY;
 #pragma unroll
@@ -166,67 +224,77 @@ __global__ __launch_bounds__(BS * 2) void prefill_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        float x = sacc[kt][r] * sl2;
-        if (diag && key > qloc) x = -INFINITY;
-        sacc[kt][r] = x;
-        mblk = fmaxf(mblk, x);
+        if (diag && key > qloc) sacc[kt][r] = -INFINITY;
+        mblk = fmaxf(mblk, sacc[kt][r]);
       }
-    mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64));
-    const float m_new = fmaxf(m_run, mblk);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);  // m_run = -inf -> 0
-    float psum = 0.f;
+    mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64)) * sl2;
+    const bool raise = mblk > m_ref + kRescale;
+    if (__ballot(raise)) {
+      const float m_new = raise ? mblk : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(sacc[kt][r] - m_use);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sl2, -m_use));
         sacc[kt][r] = p;
-        psum += p;
+        l_part += p;
       }
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
 
     // O^T += V^T P^T, 16 keys per k-step
 #pragma unroll
     for (int s = 0; s < BS / 16; ++s) {
       const int kt = s >> 1, u = s & 1;
-      // P^T k-slots 0-3 hold keys 16s + 4hi + i (registers 8u + i) and slots 4-7 keys
-      // 16s + 8 + 4hi + i (registers 8u + 4 + i): registers 8u .. 8u + 7 in order
+      // P^T k-slots 0-3: keys 16s + 4hi + i (registers 8u + i); slots 4-7: keys
+      // 16s + 8 + 4hi + i (registers 8u + 4 + i) -- registers 8u .. 8u + 7 in order
       u32x4 pw;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] = pack_bf16(sacc[kt][8 * u + 2 * i], sacc[kt][8 * u + 2 * i + 1]);
+      for (int i = 0; i < 4; ++i) pw[i] = cvt_pk_bf16(sacc[kt][8 * u + 2 * i], sacc[kt][8 * u + 2 * i + 1]);
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      // V^T operand (row d = dt*32 + l32, same key slots) through the transpose read:
+      // lane (group G, index i) addresses key row 16s + 4(G/2) + i/4 [+8], channels
+      // dt*32 + (G%2)*16 + 4(i%4) .. +3; the hardware hands each lane its column
+      const int vrow = 16 * s + 4 * (grp16 >> 1) + (i16 >> 2);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vr = &sV[(dt * 32 + l32) * VROW + 16 * s + 4 * hi];
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 8);
+        const int col = dt * 32 + (grp16 & 1) * 16 + 4 * (i16 & 3);
+        const int chunk = col >> 3, within = (col & 7) * 2;
+        const u32x2 v0 = lds_read_tr(&sV[Tile::phys(vrow, chunk) + within]);
+        const u32x2 v1 = lds_read_tr(&sV[Tile::phys(vrow + 8, chunk) + within]);
         u32x4 vw = {v0[0], v0[1], v1[0], v1[1]};
         acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
                                                              acc_o[dt], 0, 0, 0);
       }
     }
+    // (C) every wave is done with sV: start V_{n+1}
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    if (more) Tile::issue(vbase + static_cast<int64_t>(Jn) * BS * D, sV, wid, lane);
+    t = tn;
   }
 
   // normalise and store: lane holds query qloc, channels dt*32 + 8j + 4hi + i
+  const float l_run = l_part + __shfl_xor(l_part, 32, 64);
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   uint16_t* op = out + (qrow0 + qloc) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x2 w = {pack_bf16(acc_o[dt][4 * j + 0] * inv, acc_o[dt][4 * j + 1] * inv),
-                 pack_bf16(acc_o[dt][4 * j + 2] * inv, acc_o[dt][4 * j + 3] * inv)};
+      u32x2 w = {cvt_pk_bf16(acc_o[dt][4 * j + 0] * inv, acc_o[dt][4 * j + 1] * inv),
+                 cvt_pk_bf16(acc_o[dt][4 * j + 2] * inv, acc_o[dt][4 * j + 3] * inv)};
       *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * j + 4 * hi) = w;
     }
   if (lse && hi == 0)
-    lse[qrow0 + qloc] = (l_run > 0.f) ? (m_run * kLn2 + logf(l_run)) : -INFINITY;
+    lse[qrow0 + qloc] = (l_run > 0.f) ? (m_ref * kLn2 + logf(l_run)) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ plain kernel (fp32)
