@@ -53,19 +53,19 @@ __device__ __forceinline__ void prefill_work_item(int x, int nwg, int B, int Hq,
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-// LDS tile: BS rows (keys) x D bf16, row-major, rows unpadded; the 16-byte
+// LDS tile: ROWS rows (keys) x D bf16, row-major, rows unpadded; the 16-byte
 // chunk c of row r sits at chunk position c ^ (r % CPR) (XOR swizzle), so the
 // 32 rows one MFMA operand read touches spread over the banks.  Tiles are
 // filled by direct-to-LDS loads (global_load_lds_dwordx4): one wave
 // instruction writes 1 KB of consecutive LDS bytes, lane i its 16 bytes at
 // offset 16 i, and each lane fetches the global chunk that belongs there.
-template <int D, int BS>
-struct PrefillTile {
+template <int D, int ROWS, int NW>
+struct LdsTile {
   static constexpr int ROWB = D * 2;                 // bytes per row
   static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
-  static constexpr int BYTES = BS * ROWB;
-  static constexpr int NW = BS / 32;                 // waves per work-group
+  static constexpr int BYTES = ROWS * ROWB;
   static constexpr int LPW = BYTES / 1024 / NW;      // load instructions per wave per tile
+  static_assert(LPW * NW * 1024 == BYTES, "tile must split evenly over the waves");
 
   static __device__ __forceinline__ int phys(int row, int chunk) {
     return row * ROWB + ((chunk ^ (row % CPR)) << 4);
@@ -108,30 +108,123 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// One work-group per (b, h, I) with one wave per 32 queries.  Per selected key
-// block J the work-group streams K_J and V_J into LDS asynchronously in a
-// ping-pong: K_{n+1} loads while block n's softmax and P V run, V_{n+1} loads
-// while block n+1's S runs.  Each wave:
-//   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16; A = K from LDS, B = Q^T in registers)
-//   softmax on the accumulators (base 2, scale folded into one FMA); the
-//   running reference max is raised only when a block's max exceeds it by more
-//   than 8 (then O and l are rescaled), so p <= 2^8
-//   O^T += V^T P^T (A = V^T read from the row-major V tile with the LDS
-//   transpose read ds_read_b64_tr_b16; B = P^T straight from the S^T registers)
+// Per-lane state of the online softmax of one wave (32 queries, one per lane
+// column; lanes l and l ^ 32 hold the two key halves of the same query).
+template <int DT>
+struct SoftmaxState {
+  f32x16 acc_o[DT];
+  float m_ref;   // reference max (base 2)
+  float l_part;  // this lane's half of the denominator
+};
+
+// One 64-key chunk: S^T = K Q^T, masked and exponentiated in place, then
+// O^T += V^T P^T.  kbuf / vbuf hold the chunk's K and V rows (swizzled).
+template <int D>
+__device__ __forceinline__ void prefill_chunk(const uint8_t* kbuf, const uint8_t* vbuf,
+                                              const bf16x8 (&qf)[D / 16],
+                                              SoftmaxState<D / 32>& st, float sl2, int key0,
+                                              int qloc, bool diag, int l32, int hi, int grp16,
+                                              int i16) {
+  using Tile = LdsTile<D, 64, 1>;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr float kRescale = 8.f;
+  f32x16 sacc[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint4 w = *reinterpret_cast<const uint4*>(&kbuf[Tile::phys(kt * 32 + l32, 2 * s + hi)]);
+      u32x4 t = {w.x, w.y, w.z, w.w};
+      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, t), qf[s],
+                                                          sacc[kt], 0, 0, 0);
+    }
+  float mblk = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (diag && key0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) > qloc) sacc[kt][r] = -INFINITY;
+      mblk = fmaxf(mblk, sacc[kt][r]);
+    }
+  mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64)) * sl2;
+  const bool raise = mblk > st.m_ref + kRescale;
+  if (__ballot(raise)) {
+    const float m_new = raise ? mblk : st.m_ref;
+    const float alpha = (st.m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
+    st.l_part *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc_o[dt][r] *= alpha;
+    st.m_ref = m_new;
+  }
+  const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sl2, -m_use));
+      sacc[kt][r] = p;
+      st.l_part += p;
+    }
+  // O^T += V^T P^T, 16 keys per k-step.  P^T k-slots 0-3 hold keys 16s + 4hi + i
+  // (registers 8u + i of tile s/2), slots 4-7 keys 16s + 8 + 4hi + i (registers
+  // 8u + 4 + i): registers 8u .. 8u + 7 in order.  The V^T operand (row d = dt*32 +
+  // l32, the same key slots) comes from the transpose read: lane (group G, index i)
+  // addresses key row 16s + 4(G/2) + i/4 [+8] at channels dt*32 + (G%2)*16 + 4(i%4),
+  // and the hardware hands each lane its own column.
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int kt = s >> 1, u = s & 1;
+    u32x4 pw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pw[i] = cvt_pk_bf16(sacc[kt][8 * u + 2 * i], sacc[kt][8 * u + 2 * i + 1]);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+    const int vrow = 16 * s + 4 * (grp16 >> 1) + (i16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int col = dt * 32 + (grp16 & 1) * 16 + 4 * (i16 & 3);
+      const int chunk = col >> 3, within = (col & 7) * 2;
+      const u32x2 v0 = lds_read_tr(&vbuf[Tile::phys(vrow, chunk) + within]);
+      const u32x2 v1 = lds_read_tr(&vbuf[Tile::phys(vrow + 8, chunk) + within]);
+      u32x4 vw = {v0[0], v0[1], v1[0], v1[1]};
+      st.acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
+                                                              st.acc_o[dt], 0, 0, 0);
+    }
+  }
+}
+
+// One work-group per (b, h, I), one wave per 32 queries.  The selected key
+// blocks are walked as 64-key chunks; chunk c's K and V rows live in LDS
+// buffer c % 2 and chunk c + 1 streams into the other buffer (direct-to-LDS,
+// asynchronous) while chunk c is computed, so loads overlap the matrix work.
+// The loop is unrolled by two so each half names its buffers statically.
+// Per chunk each wave computes S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K
+// from LDS, B = Q^T in registers), the online softmax on the accumulators
+// (base 2, scale folded into one FMA, the reference max raised only when a
+// chunk exceeds it by more than 8, so p <= 2^8), and O^T += V^T P^T with P^T
+// taken straight from the S^T registers and V^T from the LDS transpose read.
 template <int D, int BS>
 __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int B, int Hq, int Hkv, int S, const int32_t* __restrict__ blk_idx,
     const int32_t* __restrict__ blk_cnt, int max_sel, int causal, float scale,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  using Tile = PrefillTile<D, BS>;
-  constexpr int KS = D / 16;          // k-steps of the QK^T product
-  constexpr int KT = BS / 32;         // 32-key tiles per block
-  constexpr int DT = D / 32;          // 32-wide d tiles of the output
-  constexpr int LPW = Tile::LPW;
-  constexpr float kRescale = 8.f;     // lazy-rescale threshold (base-2 units)
-  __shared__ __attribute__((aligned(1024))) uint8_t sK[Tile::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV[Tile::BYTES];
+  constexpr int NW = BS / 32;
+  using Tile = LdsTile<D, 64, NW>;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int CPB = BS / 64;         // 64-key chunks per block
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[Tile::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[Tile::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[Tile::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[Tile::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -174,127 +267,70 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
   }
   const float sl2 = scale * kLog2e;
-
-  f32x16 acc_o[DT];
+  SoftmaxState<DT> st;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
-  float m_ref = -INFINITY;  // reference max (base 2) of this lane's query
-  float l_part = 0.f;       // this lane's half of the softmax denominator
+    for (int r = 0; r < 16; ++r) st.acc_o[dt][r] = 0.f;
+  st.m_ref = -INFINITY;
+  st.l_part = 0.f;
 
-  int t = next_valid(0);
-  if (t < cnt) {
-    Tile::issue(kbase + static_cast<int64_t>(sel[t]) * BS * D, sK, wid, lane);
-    Tile::issue(vbase + static_cast<int64_t>(sel[t]) * BS * D, sV, wid, lane);
-  }
+  // chunk cursor: list position t, chunk c within the block
+  int t = next_valid(0), c = 0;
+  auto issue_chunk = [&](int tt, int cc, uint8_t* kb, uint8_t* vb) {
+    const int64_t row0 = static_cast<int64_t>(sel[tt]) * BS + cc * 64;
+    Tile::issue(kbase + row0 * D, kb, wid, lane);
+    Tile::issue(vbase + row0 * D, vb, wid, lane);
+  };
+  auto advance = [&](int& tt, int& cc) {
+    if (cc + 1 < CPB) { ++cc; } else { tt = next_valid(tt + 1); cc = 0; }
+  };
+  // Per chunk: wait for this wave's share of chunk c, barrier (every share has
+  // landed and every wave has finished chunk c - 1, whose buffers are free),
+  // issue chunk c + 1 into those buffers, compute chunk c.
+  if (t < cnt) issue_chunk(t, c, sK0, sV0);
   while (t < cnt) {
-    const int J = sel[t];
-    const int tn = next_valid(t + 1);
-    const bool more = tn < cnt;
-    const int Jn = more ? sel[tn] : 0;
-    // (A) K_n has landed for every wave
-    wait_vmcnt<LPW>();
-    __builtin_amdgcn_s_barrier();
-
-    f32x16 sacc[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&sK[Tile::phys(kt * 32 + l32, 2 * s + hi)]);
-        u32x4 t = {w.x, w.y, w.z, w.w};
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, t), qf[s],
-                                                            sacc[kt], 0, 0, 0);
-      }
+    // ---- even half: chunk in buffers 0, next chunk into buffers 1
+    {
+      int tn = t, cn = c;
+      advance(tn, cn);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (tn < cnt) issue_chunk(tn, cn, sK1, sV1);
+      const int J = sel[t];
+      prefill_chunk<D>(sK0, sV0, qf, st, sl2, c * 64, qloc, causal && J == I, l32, hi, grp16, i16);
+      t = tn;
+      c = cn;
     }
-    // (B) every wave is done with sK and V_n has landed: start K_{n+1}
-    wait_lgkm0();
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (more) Tile::issue(kbase + static_cast<int64_t>(Jn) * BS * D, sK, wid, lane);
-
-    // softmax: block max per query (this lane's 16 keys per tile and lane ^ 32)
-    const bool diag = causal && (J == I);
-    float mblk = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (diag && key > qloc) sacc[kt][r] = -INFINITY;
-        mblk = fmaxf(mblk, sacc[kt][r]);
-      }
-    mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64)) * sl2;
-    const bool raise = mblk > m_ref + kRescale;
-    if (__ballot(raise)) {
-      const float m_new = raise ? mblk : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
-      m_ref = m_new;
+    if (t >= cnt) break;
+    // ---- odd half: chunk in buffers 1, next chunk into buffers 0
+    {
+      int tn = t, cn = c;
+      advance(tn, cn);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (tn < cnt) issue_chunk(tn, cn, sK0, sV0);
+      const int J = sel[t];
+      prefill_chunk<D>(sK1, sV1, qf, st, sl2, c * 64, qloc, causal && J == I, l32, hi, grp16, i16);
+      t = tn;
+      c = cn;
     }
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sl2, -m_use));
-        sacc[kt][r] = p;
-        l_part += p;
-      }
-
-    // O^T += V^T P^T, 16 keys per k-step
-#pragma unroll
-    for (int s = 0; s < BS / 16; ++s) {
-      const int kt = s >> 1, u = s & 1;
-      // P^T k-slots 0-3: keys 16s + 4hi + i (registers 8u + i); slots 4-7: keys
-      // 16s + 8 + 4hi + i (registers 8u + 4 + i) -- registers 8u .. 8u + 7 in order
-      u32x4 pw;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] = cvt_pk_bf16(sacc[kt][8 * u + 2 * i], sacc[kt][8 * u + 2 * i + 1]);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-      // V^T operand (row d = dt*32 + l32, same key slots) through the transpose read:
-      // lane (group G, index i) addresses key row 16s + 4(G/2) + i/4 [+8], channels
-      // dt*32 + (G%2)*16 + 4(i%4) .. +3; the hardware hands each lane its column
-      const int vrow = 16 * s + 4 * (grp16 >> 1) + (i16 >> 2);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int col = dt * 32 + (grp16 & 1) * 16 + 4 * (i16 & 3);
-        const int chunk = col >> 3, within = (col & 7) * 2;
-        const u32x2 v0 = lds_read_tr(&sV[Tile::phys(vrow, chunk) + within]);
-        const u32x2 v1 = lds_read_tr(&sV[Tile::phys(vrow + 8, chunk) + within]);
-        u32x4 vw = {v0[0], v0[1], v1[0], v1[1]};
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
-                                                             acc_o[dt], 0, 0, 0);
-      }
-    }
-    // (C) every wave is done with sV: start V_{n+1}
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    if (more) Tile::issue(vbase + static_cast<int64_t>(Jn) * BS * D, sV, wid, lane);
-    t = tn;
   }
 
   // normalise and store: lane holds query qloc, channels dt*32 + 8j + 4hi + i
-  const float l_run = l_part + __shfl_xor(l_part, 32, 64);
+  const float l_run = st.l_part + __shfl_xor(st.l_part, 32, 64);
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   uint16_t* op = out + (qrow0 + qloc) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x2 w = {cvt_pk_bf16(acc_o[dt][4 * j + 0] * inv, acc_o[dt][4 * j + 1] * inv),
-                 cvt_pk_bf16(acc_o[dt][4 * j + 2] * inv, acc_o[dt][4 * j + 3] * inv)};
+      u32x2 w = {cvt_pk_bf16(st.acc_o[dt][4 * j + 0] * inv, st.acc_o[dt][4 * j + 1] * inv),
+                 cvt_pk_bf16(st.acc_o[dt][4 * j + 2] * inv, st.acc_o[dt][4 * j + 3] * inv)};
       *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * j + 4 * hi) = w;
     }
   if (lse && hi == 0)
-    lse[qrow0 + qloc] = (l_run > 0.f) ? (m_ref * kLn2 + logf(l_run)) : -INFINITY;
+    lse[qrow0 + qloc] = (l_run > 0.f) ? (st.m_ref * kLn2 + logf(l_run)) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ plain kernel (fp32)
