@@ -7,7 +7,7 @@ same name.  All computation happens in the HIP kernels.  If the shared
 library has not been built, importing this package raises ImportError; there
 is no CPU fallback.
 
-Build: ``python -m long_context_sparse_apply_amd.build``.
+Build: ``python long_context_sparse_apply_amd/build.py``.
 """
 from __future__ import annotations
 
@@ -35,7 +35,7 @@ class SAError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run python -m long_context_sparse_apply_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run python long_context_sparse_apply_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, I64, D, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double,
                            ctypes.c_float, ctypes.c_size_t)

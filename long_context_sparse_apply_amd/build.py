@@ -1,6 +1,6 @@
 """Build the gfx950 shared library in-tree with hipcc.
 
-    python -m long_context_sparse_apply_amd.build
+    python long_context_sparse_apply_amd/build.py      (or __graft_entry__.build())
 
 Each source compiles to an object under ``_build/`` (in parallel), then one
 link produces ``long_context_sparse_apply_amd/libsa_mi355x.so``.  A build

@@ -54,11 +54,14 @@ __device__ __forceinline__ void prefill_work_item(int x, int nwg, int B, int Hq,
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 // LDS tile: ROWS rows (keys) x D bf16, row-major, rows unpadded; the 16-byte
-// chunk c of row r sits at chunk position c ^ (r % CPR) (XOR swizzle), so the
-// 32 rows one MFMA operand read touches spread over the banks.  Tiles are
-// filled by direct-to-LDS loads (global_load_lds_dwordx4): one wave
-// instruction writes 1 KB of consecutive LDS bytes, lane i its 16 bytes at
-// offset 16 i, and each lane fetches the global chunk that belongs there.
+// chunk c of row r sits at chunk position c ^ sw(r), with
+// sw(r) = 2 (r mod CPR/2) + (r div CPR/2 mod 2).  sw is one-to-one on r mod CPR,
+// so the 16 consecutive rows of a K operand read land on 16 distinct bank
+// groups; and for the 4 consecutive rows x 2 adjacent chunks of a V transpose
+// read it yields 8 distinct positions.  Tiles are filled by direct-to-LDS
+// loads (global_load_lds_dwordx4): one wave instruction writes 1 KB of
+// consecutive LDS bytes, lane i its 16 bytes at offset 16 i, and each lane
+// fetches the global chunk that belongs there.
 template <int D, int ROWS, int NW>
 struct LdsTile {
   static constexpr int ROWB = D * 2;                 // bytes per row
@@ -67,8 +70,11 @@ struct LdsTile {
   static constexpr int LPW = BYTES / 1024 / NW;      // load instructions per wave per tile
   static_assert(LPW * NW * 1024 == BYTES, "tile must split evenly over the waves");
 
+  static __device__ __forceinline__ int sw(int row) {
+    return ((row % (CPR / 2)) << 1) | ((row / (CPR / 2)) & 1);
+  }
   static __device__ __forceinline__ int phys(int row, int chunk) {
-    return row * ROWB + ((chunk ^ (row % CPR)) << 4);
+    return row * ROWB + ((chunk ^ sw(row)) << 4);
   }
   // issue this wave's share of the tile's direct-to-LDS loads (asynchronous)
   static __device__ __forceinline__ void issue(const uint16_t* g, uint8_t* lds, int wid, int lane) {
@@ -78,9 +84,9 @@ struct LdsTile {
       const int off = ins * 1024 + lane * 16;
       const int row = off / ROWB;
       const int pos = (off % ROWB) >> 4;
-      const int chunk = pos ^ (row % CPR);
+      const int chunk = pos ^ sw(row);
       const uint8_t* src = reinterpret_cast<const uint8_t*>(g) + row * ROWB + chunk * 16;
-      __builtin_amdgcn_global_load_lds(src, lds + ins * 1024, 16, 0, 0);
+      lds_dma16(src, lds + ins * 1024);
     }
   }
 };

@@ -95,6 +95,15 @@ __device__ __forceinline__ void rot_cos_sin(int64_t p, double f, float& c, float
   sincosf(ang, &s, &c);
 }
 
+// ---------------------------------------------------------------- direct-to-LDS load
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i of the wave writes lds_wave_base + 16 i; lds_wave_base must be uniform.
+// Completion is tracked by vmcnt.  Kept in a __device__ function so host
+// compilation of the calling kernels never sees the builtin.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -7,112 +7,170 @@
 //
 //   s(b, h, t) = scale * sum_{i in D_g} (q_i k_{t,i} + q_{i+P} k_{t,i+P})
 //
-// One work-group streams 256 cached tokens of one (batch, KV head) and scores
-// them for all Hq/Hkv query heads of the group, so every key byte is read once
-// per group.  A token row is split over LPT lanes that each load 16 bytes
-// (8 channels, bf16): in the standard layout the whole d-channel row is read
-// (the dominant pairs are scattered through it) and multiplied by a query whose
-// non-dominant channels are zero; in the slab layout only the 2*n_dom dominant
-// channels are stored contiguously and read.  Per-lane partial dots are summed
-// across the LPT lanes with xor shuffles; scores are staged in LDS and written
-// as contiguous rows.
+// A work-group walks a range of cached tokens of one (batch, KV head) in
+// chunks of CT tokens and scores them for all Hq/Hkv query heads of the group,
+// so every key byte is read once per group.  Each chunk's stored rows (the
+// whole d-channel row in the standard layout, where the dominant pairs are
+// scattered through it; only the 2*n_dom-channel dominant slab otherwise)
+// stream into LDS with direct-to-LDS loads, double-buffered: chunk c + 1 loads
+// while chunk c is scored.  Row r's 16-byte chunk j sits at chunk position
+// j ^ (r % CPR).  A thread scores one token for its share of the query heads:
+// it reads the token's dominant channels from LDS once (2-byte reads in the
+// standard layout, 16-byte reads of the slab) and takes the query slices,
+// staged once per work-group in LDS, as broadcast reads.
 #include "sa_common.hpp"
 
 namespace sa {
 
-constexpr int kTokPerWG = 256;
+template <typename T> struct TokElem;
+template <> struct TokElem<uint16_t> {
+  static __device__ __forceinline__ float lds(const uint8_t* p) {
+    return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
+  }
+};
+template <> struct TokElem<float> {
+  static __device__ __forceinline__ float lds(const uint8_t* p) {
+    return *reinterpret_cast<const float*>(p);
+  }
+};
 
-template <typename T, int ROW, int GRP>
+// ROW: channels per stored row (d, or 2*n_dom for the slab); NDC: dominant
+// channels per head (2*n_dom) rounded up; GRP: query heads per KV head.
+template <typename T, int ROW, int GRP, int NDC>
+struct TokenScoreShape {
+  static constexpr int ES = static_cast<int>(sizeof(T));
+  static constexpr int ROWB = ROW * ES;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int CT0 = 32768 / ROWB;
+  static constexpr int CT = CT0 < 256 ? CT0 : 256;           // tokens per chunk
+  static constexpr int HGS0 = 256 / CT;                        // threads per token
+  static constexpr int HGS = HGS0 < GRP ? HGS0 : GRP;
+  static constexpr int HPT = GRP / HGS;                        // heads per thread
+  static constexpr int CHB = CT * ROWB;                        // chunk bytes
+  static constexpr int LPW = CHB / 1024 / 4;                   // DMA per wave per chunk
+  static_assert(LPW * 4096 == CHB, "chunk must split over 4 waves");
+};
+
+template <typename T, int ROW, int GRP, int NDC, bool SLAB>
 __global__ __launch_bounds__(256) void token_score_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int Hq, int Hkv, int Lmax, int d,
-    const int32_t* __restrict__ cache_len, const int32_t* __restrict__ dom, int n_dom, int slab,
-    float scale, float* __restrict__ scores) {
-  constexpr int LPT = ROW / 8;          // lanes per token row
-  constexpr int TPI = kWave / LPT;      // tokens per wave per step
-  constexpr int WAVES = 256 / kWave;
+    const int32_t* __restrict__ cache_len, const int32_t* __restrict__ dom, int n_dom,
+    float scale, float* __restrict__ scores, int chunks_per_wg) {
+  using Sh = TokenScoreShape<T, ROW, GRP, NDC>;
+  constexpr int ES = Sh::ES, ROWB = Sh::ROWB, CPR = Sh::CPR, CT = Sh::CT, HPT = Sh::HPT;
+  constexpr int CHB = Sh::CHB, LPW = Sh::LPW;
+  static_assert(!SLAB || ROW == NDC, "the slab row is exactly the dominant channels");
+  __shared__ __attribute__((aligned(1024))) uint8_t sk0[CHB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk1[CHB];
+  __shared__ __attribute__((aligned(16))) float s_q[GRP][NDC];
+  __shared__ int s_off[NDC];
+
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
-  const int sub = lane % LPT;
-  const int tok_in_step = lane / LPT;
-  const int t0 = blockIdx.x * kTokPerWG;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int P = d / 2;
   const int L = cache_len[b];
+  const int ndc = 2 * n_dom;
+  const int tb = blockIdx.x * chunks_per_wg * CT;                   // first token of this WG
+  int nch = (Lmax - tb + CT - 1) / CT;
+  nch = nch < chunks_per_wg ? nch : chunks_per_wg;
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(k + (static_cast<int64_t>(b) * Hkv + g) * Lmax * ROW);
 
-  __shared__ float s_q[GRP][128];
-  __shared__ uint64_t s_dmask;
-  __shared__ int s_ch[128];
-  __shared__ float s_out[GRP][kTokPerWG];
-
-  // channel held by slab/row position c, and the dominant-pair mask
-  if (tid == 0) {
-    uint64_t m = 0;
-    for (int j = 0; j < n_dom; ++j) m |= 1ull << dom[g * n_dom + j];
-    s_dmask = m;
-  }
-  __syncthreads();
-  if (tid < ROW) {
-    int ch = tid;
-    if (slab) {
-      const int j = tid % n_dom;
-      ch = dom[g * n_dom + j] + (tid >= n_dom ? P : 0);
+  // stage chunk c's rows (rows past the cache end re-read its last row)
+  auto issue = [&](int c, uint8_t* buf) {
+    const int t0 = tb + c * CT;
+    const int last = Lmax - 1 - t0;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int ins = wid * LPW + j;
+      const int off = ins * 1024 + lane * 16;
+      const int row = off / ROWB;
+      const int pos = (off % ROWB) >> 4;
+      const int src_row = row < last ? row : last;
+      lds_dma16(kb + static_cast<int64_t>(t0 + src_row) * ROWB + ((pos ^ (row % CPR)) << 4),
+                buf + ins * 1024);
     }
-    s_ch[tid] = ch;
-  }
-  __syncthreads();
-  for (int e = tid; e < GRP * ROW; e += 256) {
-    const int hh = e / ROW, c = e % ROW;
-    const int ch = s_ch[c];
-    const int pair = ch % P;
-    const bool dominant = (s_dmask >> pair) & 1ull;
-    const float v = Elem<T>::load1(q + (static_cast<int64_t>(b) * Hq + g * GRP + hh) * d + ch);
-    s_q[hh][c] = dominant ? v : 0.f;
-  }
-  __syncthreads();
-  float qv[GRP][8];
-#pragma unroll
-  for (int hh = 0; hh < GRP; ++hh)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qv[hh][j] = s_q[hh][sub * 8 + j];
+  };
+  if (nch > 0) issue(0, sk0);
 
-  const T* kb = k + (static_cast<int64_t>(b) * Hkv + g) * static_cast<int64_t>(Lmax) * ROW;
-  constexpr int STEPS = kTokPerWG / (WAVES * TPI);
-#pragma unroll 4
-  for (int it = 0; it < STEPS; ++it) {
-    const int tl = (it * WAVES + wid) * TPI + tok_in_step;  // token within the work-group
-    const int t = t0 + tl;
-    float kv[8];
-    const bool live = t < L;
-    if (live) {
-      Elem<T>::load8(kb + static_cast<int64_t>(t) * ROW + sub * 8, kv);
+  // query slices (dominant channels, pre-scaled) and the stored channel of each
+  for (int e = tid; e < GRP * NDC; e += 256) {
+    const int hh = e / NDC, j = e % NDC;
+    float v = 0.f;
+    if (j < ndc) {
+      const int qc = dom[g * n_dom + (j % n_dom)] + (j >= n_dom ? P : 0);
+      v = Elem<T>::load1(q + (static_cast<int64_t>(b) * Hq + g * GRP + hh) * d + qc) * scale;
+    }
+    s_q[hh][j] = v;
+  }
+  if (tid < NDC) {
+    int c = 0;
+    if (tid < ndc) c = SLAB ? tid : dom[g * n_dom + (tid % n_dom)] + (tid >= n_dom ? P : 0);
+    s_off[tid] = c * ES;  // byte offset of the channel within an unswizzled row
+  }
+
+  const int r = tid % CT;              // this thread's token within a chunk
+  const int hg = tid / CT;             // its head group (HGS groups of HPT heads)
+  const bool active = hg * HPT < GRP;
+  const int rx = r % CPR;
+
+  auto score_chunk = [&](int c, const uint8_t* buf) {
+    if (!active) return;
+    const int t = tb + c * CT + r;
+    const uint8_t* rowp = buf + r * ROWB;
+    float kv[NDC];
+    if constexpr (SLAB) {
+#pragma unroll
+      for (int j = 0; j < CPR; ++j) {
+        const uint4 w = *reinterpret_cast<const uint4*>(rowp + ((j ^ rx) << 4));
+        float tmp[8];
+        if constexpr (ES == 2) {
+          Elem<uint16_t>::unpack8(w, tmp);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kv[j * 8 + e] = tmp[e];
+        } else {
+          kv[j * 4 + 0] = __uint_as_float(w.x); kv[j * 4 + 1] = __uint_as_float(w.y);
+          kv[j * 4 + 2] = __uint_as_float(w.z); kv[j * 4 + 3] = __uint_as_float(w.w);
+        }
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) kv[j] = 0.f;
-    }
-    float acc[GRP];
-#pragma unroll
-    for (int hh = 0; hh < GRP; ++hh) {
-      float a = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a = fmaf(qv[hh][j], kv[j], a);
-      acc[hh] = a;
+      for (int j = 0; j < NDC; ++j) {
+        const int byte = s_off[j];
+        kv[j] = TokElem<T>::lds(rowp + ((((byte >> 4) ^ rx)) << 4) + (byte & 15));
+      }
     }
 #pragma unroll
-    for (int o = LPT / 2; o >= 1; o >>= 1)
+    for (int u = 0; u < HPT; ++u) {
+      const int hh = hg * HPT + u;
+      float acc = 0.f;
 #pragma unroll
-      for (int hh = 0; hh < GRP; ++hh) acc[hh] += __shfl_xor(acc[hh], o, kWave);
-#pragma unroll
-    for (int hh = 0; hh < GRP; ++hh)
-      if (hh % LPT == sub) s_out[hh][tl] = live ? scale * acc[hh] : -INFINITY;
-  }
-  __syncthreads();
-  for (int e = tid; e < GRP * kTokPerWG; e += 256) {
-    const int hh = e / kTokPerWG, tl = e % kTokPerWG;
-    const int t = t0 + tl;
-    if (t < Lmax)
-      scores[(static_cast<int64_t>(b) * Hq + g * GRP + hh) * Lmax + t] = s_out[hh][tl];
+      for (int j = 0; j < NDC; j += 4) {
+        const float4 qv = *reinterpret_cast<const float4*>(&s_q[hh][j]);
+        acc = fmaf(qv.x, kv[j], acc);
+        acc = fmaf(qv.y, kv[j + 1], acc);
+        acc = fmaf(qv.z, kv[j + 2], acc);
+        acc = fmaf(qv.w, kv[j + 3], acc);
+      }
+      if (t < Lmax)
+        scores[(static_cast<int64_t>(b) * Hq + g * GRP + hh) * Lmax + t] = (t < L) ? acc : -INFINITY;
+    }
+  };
+
+  // wait for chunk c, barrier (every share landed; every thread is done with
+  // chunk c - 1, whose buffer is free), issue chunk c + 1, score chunk c
+  for (int c = 0; c < nch; c += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c + 1 < nch) issue(c + 1, sk1);
+    score_chunk(c, sk0);
+    if (c + 1 >= nch) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c + 2 < nch) issue(c + 2, sk0);
+    score_chunk(c + 1, sk1);
   }
 }
 
@@ -121,34 +179,59 @@ hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, in
                               int n_dom, int slab, float scale, float* scores, hipStream_t st) {
   const int row = slab ? 2 * n_dom : d;
   const int grp = Hq / Hkv;
-  const dim3 grid((Lmax + kTokPerWG - 1) / kTokPerWG, Hkv, B);
-#define SA_TS(T, R, G)                                                                       \
-  token_score_kernel<T, R, G><<<grid, 256, 0, st>>>(static_cast<const T*>(q),                \
-                                                    static_cast<const T*>(k), Hq, Hkv, Lmax, d, \
-                                                    cache_len, dom, n_dom, slab, scale, scores)
-#define SA_TS_G(T, R)                      \
-  switch (grp) {                           \
-    case 1: SA_TS(T, R, 1); break;         \
-    case 2: SA_TS(T, R, 2); break;         \
-    case 4: SA_TS(T, R, 4); break;         \
-    case 8: SA_TS(T, R, 8); break;         \
-    default: return hipErrorInvalidValue;  \
+  const int ndc_need = 2 * n_dom;
+  const int ndc = ndc_need <= 8 ? 8 : ndc_need <= 16 ? 16 : ndc_need <= 32 ? 32 : ndc_need <= 64 ? 64 : 128;
+  const int es = dtype == kBF16 ? 2 : 4;
+  const int ct0 = 32768 / (row * es);
+  const int ct = ct0 < 256 ? ct0 : 256;
+  // about 4096 tokens per work-group, fewer when that leaves under ~2048 work-groups
+  const int per_head_chunks = (Lmax + ct - 1) / ct;
+  int cpw = 4096 / ct;
+  while (cpw > 1 && static_cast<int64_t>(B) * Hkv * ((per_head_chunks + cpw - 1) / cpw) < 2048) cpw /= 2;
+  const dim3 grid((per_head_chunks + cpw - 1) / cpw, Hkv, B);
+#define SA_TS(T, R, G, C, SL)                                                                 \
+  token_score_kernel<T, R, G, C, SL><<<grid, 256, 0, st>>>(static_cast<const T*>(q),            \
+                                                           static_cast<const T*>(k), Hq, Hkv, Lmax, \
+                                                           d, cache_len, dom, n_dom, scale, scores, cpw)
+#define SA_TS_G(T, R, C, SL)                  \
+  switch (grp) {                              \
+    case 1: SA_TS(T, R, 1, C, SL); break;     \
+    case 2: SA_TS(T, R, 2, C, SL); break;     \
+    case 4: SA_TS(T, R, 4, C, SL); break;     \
+    case 8: SA_TS(T, R, 8, C, SL); break;     \
+    default: return hipErrorInvalidValue;     \
   }
-#define SA_TS_R(T)                                \
-  switch (row) {                                  \
-    case 8: SA_TS_G(T, 8) break;                  \
-    case 16: SA_TS_G(T, 16) break;                \
-    case 32: SA_TS_G(T, 32) break;                \
-    case 64: SA_TS_G(T, 64) break;                \
-    case 128: SA_TS_G(T, 128) break;              \
-    default: return hipErrorInvalidValue;         \
+#define SA_TS_STD(T, D)                             \
+  switch (ndc) {                                    \
+    case 8: SA_TS_G(T, D, 8, false) break;          \
+    case 16: SA_TS_G(T, D, 16, false) break;        \
+    case 32: SA_TS_G(T, D, 32, false) break;        \
+    case 64: SA_TS_G(T, D, 64, false) break;        \
+    default: SA_TS_G(T, D, 128, false) break;       \
+  }
+#define SA_TS_DT(T)                                                    \
+  if (slab) {                                                          \
+    switch (row) {                                                     \
+      case 8: SA_TS_G(T, 8, 8, true) break;                            \
+      case 16: SA_TS_G(T, 16, 16, true) break;                         \
+      case 32: SA_TS_G(T, 32, 32, true) break;                         \
+      case 64: SA_TS_G(T, 64, 64, true) break;                         \
+      case 128: SA_TS_G(T, 128, 128, true) break;                      \
+      default: return hipErrorInvalidValue;                            \
+    }                                                                  \
+  } else if (d == 128) {                                               \
+    SA_TS_STD(T, 128)                                                  \
+  } else {                                                             \
+    if (ndc > 64) return hipErrorInvalidValue;                         \
+    SA_TS_STD(T, 64)                                                   \
   }
   if (dtype == kBF16) {
-    SA_TS_R(uint16_t)
+    SA_TS_DT(uint16_t)
   } else {
-    SA_TS_R(float)
+    SA_TS_DT(float)
   }
-#undef SA_TS_R
+#undef SA_TS_DT
+#undef SA_TS_STD
 #undef SA_TS_G
 #undef SA_TS
   return hipGetLastError();

@@ -161,6 +161,10 @@ def _tricky_scores(rows, cols, seed):
         s[2, 1::2] = 0.0
         s[3, ::5] = -np.inf
         s[4, :] = -np.inf
+    if rows > 8:
+        s[6, :] = np.arange(cols, dtype=np.float32)            # best at the end
+        s[7, :] = -np.arange(cols, dtype=np.float32)           # best at the start
+        s[8, ::97] += 50.0                                     # sparse strong entries
     return s
 
 
@@ -171,7 +175,7 @@ TOPK_CASES = [  # rows, cols, k_const, n_sink, n_local, per-row valid_len, per-r
     (70, 1024, 52, 1, 2, True, True),
     (9, 1000, 0, 2, 0, True, False),
     (12, 5000, 300, 0, 0, True, False),
-    (6, 65536, 2048, 0, 0, False, False),
+    (10, 65536, 2048, 0, 0, False, False),
     (7, 131072, 4096, 0, 0, True, False),
     (5, 20000, 4500, 3, 3, True, True),
 ]
