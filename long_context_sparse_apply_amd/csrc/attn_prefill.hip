@@ -7,15 +7,16 @@
 // h / (Hq/Hkv).
 //
 // bf16 path (d in {64, 128}, block in {64, 128}): one work-group per
-// (b, h, I) with one wave per 32 queries.  For every selected key block the
-// work-group stages K (row-major) and V (transposed, [d][key]) in LDS; each
-// wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
-// B = Q^T held in registers for the whole block list), so the C layout leaves
-// one query per lane column and 16 keys per lane.  The online softmax (fp32,
-// base-2 exponent with the scale folded in) runs on those registers; the
-// probabilities are rounded to bf16 and used directly as the B operand of
-// O^T += V^T P^T (the k-slot order of P^T matches the C layout of S^T, and
-// V^T is read from LDS in the same key order), so P never leaves registers.
+// (b, h, I) with one wave per 32 queries.  The selected key blocks are walked
+// as 64-key chunks staged in LDS (K and V both row-major, swizzled) by
+// direct-to-LDS loads.  Each wave computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in registers for the
+// whole block list), so the C layout leaves one query per lane column and 16
+// keys per lane.  The online softmax (fp32, base-2 exponent with the scale
+// folded in) runs on those registers; the probabilities are rounded to bf16
+// and used directly as the B operand of O^T += V^T P^T (the k-slot order of
+// P^T matches the C layout of S^T; V^T comes from LDS transpose reads in the
+// same key order), so P never leaves registers.
 //
 // Work order: large query blocks first (their lists are the longest) and all
 // work of one KV group placed on one XCD when the grid divides evenly, so the
@@ -54,14 +55,22 @@ __device__ __forceinline__ void prefill_work_item(int x, int nwg, int B, int Hq,
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 // LDS tile: ROWS rows (keys) x D bf16, row-major, rows unpadded; the 16-byte
-// chunk c of row r sits at chunk position c ^ sw(r), with
-// sw(r) = 2 (r mod CPR/2) + (r div CPR/2 mod 2).  sw is one-to-one on r mod CPR,
-// so the 16 consecutive rows of a K operand read land on 16 distinct bank
-// groups; and for the 4 consecutive rows x 2 adjacent chunks of a V transpose
-// read it yields 8 distinct positions.  Tiles are filled by direct-to-LDS
-// loads (global_load_lds_dwordx4): one wave instruction writes 1 KB of
-// consecutive LDS bytes, lane i its 16 bytes at offset 16 i, and each lane
-// fetches the global chunk that belongs there.
+// chunk c of row r sits at chunk position c ^ sw(r).  With r = 4b + a
+// (a, b in 0..3, bits a0 a1 b0 b1), sw(r) has bits
+//   bit 0 = b0, bit 1 = a0 ^ b1, bit 2 = a1, bit 3 = a0   (bit 3 only when D = 128)
+// It depends on r mod 16 only, so rows 16 and 32 further on use the same
+// pattern.  It makes both read patterns conflict-free whether the LDS serves
+// 128 or 256 bytes a cycle:
+//  - a K operand read (16 bytes a lane, rows r..r+7 or r..r+15 at one chunk,
+//    r aligned) hits distinct 16-byte bank groups, since sw is one-to-one on
+//    (a0, a1, b0) and, for 16 rows, on r mod 16 (D = 128) or on the 8 rows of
+//    one parity (D = 64, two rows per 256 bytes);
+//  - a V transpose read (8 bytes a lane, 4 aligned rows x 2 or 4 adjacent
+//    chunks) does too, since bits 1-2 and bits 2-3 of sw are one-to-one on
+//    (a0, a1).
+// Tiles are filled by direct-to-LDS loads (global_load_lds_dwordx4): one wave
+// instruction writes 1 KB of consecutive LDS bytes, lane i its 16 bytes at
+// offset 16 i, and each lane fetches the global chunk that belongs there.
 template <int D, int ROWS, int NW>
 struct LdsTile {
   static constexpr int ROWB = D * 2;                 // bytes per row
@@ -69,9 +78,11 @@ struct LdsTile {
   static constexpr int BYTES = ROWS * ROWB;
   static constexpr int LPW = BYTES / 1024 / NW;      // load instructions per wave per tile
   static_assert(LPW * NW * 1024 == BYTES, "tile must split evenly over the waves");
+  static_assert(CPR == 8 || CPR == 16, "the swizzle is laid out for D = 64 or 128");
 
   static __device__ __forceinline__ int sw(int row) {
-    return ((row % (CPR / 2)) << 1) | ((row / (CPR / 2)) & 1);
+    const int a0 = row & 1, a1 = (row >> 1) & 1, b0 = (row >> 2) & 1, b1 = (row >> 3) & 1;
+    return (b0 | ((a0 ^ b1) << 1) | (a1 << 2) | (a0 << 3)) & (CPR - 1);
   }
   static __device__ __forceinline__ int phys(int row, int chunk) {
     return row * ROWB + ((chunk ^ sw(row)) << 4);
@@ -90,6 +101,10 @@ struct LdsTile {
     }
   }
 };
+
+// Pointer to uniform, read-only data in the constant address space (its loads
+// are scalar).
+typedef const __attribute__((address_space(4))) int32_t* uniform_i32p;
 
 // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left at their maxima (gfx9 encoding)
 template <int N>
@@ -123,42 +138,83 @@ struct SoftmaxState {
   float l_part;  // this lane's half of the denominator
 };
 
-// One 64-key chunk: S^T = K Q^T, masked and exponentiated in place, then
-// O^T += V^T P^T.  kbuf / vbuf hold the chunk's K and V rows (swizzled).
+// Per-lane LDS byte offsets of a wave's reads of a 64-key tile.  The swizzle
+// repeats every 16 rows, so one offset per (k-step) for K and per (d-tile,
+// half) for V covers every read; rows 32 (K) and 16 (V) further on are fixed
+// byte distances away and go into the instructions' immediate offsets.
 template <int D>
-__device__ __forceinline__ void prefill_chunk(const uint8_t* kbuf, const uint8_t* vbuf,
-                                              const bf16x8 (&qf)[D / 16],
-                                              SoftmaxState<D / 32>& st, float sl2, int key0,
-                                              int qloc, bool diag, int l32, int hi, int grp16,
-                                              int i16) {
-  using Tile = LdsTile<D, 64, 1>;
-  constexpr int KS = D / 16;
-  constexpr int DT = D / 32;
-  constexpr float kRescale = 8.f;
-  f32x16 sacc[2];
+struct ChunkOffsets {
+  int k[D / 16];      // K row l32, 16-byte chunk 2s + hi
+  int v[D / 32][2];   // V row 4(G/2) + i/4 (+8), channels dt*32 + (G%2)*16 + 4(i%4)
+  __device__ __forceinline__ void init(int l32, int hi, int grp16, int i16) {
+    using Tile = LdsTile<D, 64, 1>;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) k[s] = Tile::phys(l32, 2 * s + hi);
+    const int vrow = 4 * (grp16 >> 1) + (i16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int col = dt * 32 + (grp16 & 1) * 16 + 4 * (i16 & 3);
+      v[dt][0] = Tile::phys(vrow, col >> 3) + (col & 7) * 2;
+      v[dt][1] = Tile::phys(vrow + 8, col >> 3) + (col & 7) * 2;
+    }
+  }
+  // an empty asm that claims to rewrite the offsets: address arithmetic that
+  // uses them cannot be hoisted out of the caller's loop, so each read keeps
+  // the form offset-register + immediate instead of a register per address
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(k[s]));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+v"(v[dt][0]), "+v"(v[dt][1]));
+  }
+};
+
+// S^T = K Q^T for one 64-key chunk (K tile kbuf): two 32-key tiles, D/16
+// k-steps each.
+template <int D>
+__device__ __forceinline__ void chunk_scores(const uint8_t* kbuf, const ChunkOffsets<D>& off,
+                                             const bf16x8 (&qf)[D / 16], f32x16 (&sacc)[2]) {
+  constexpr int ROWB = 2 * D;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
+  for (int s = 0; s < D / 16; ++s)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const uint4 w = *reinterpret_cast<const uint4*>(&kbuf[Tile::phys(kt * 32 + l32, 2 * s + hi)]);
+      const uint4 w = *reinterpret_cast<const uint4*>(kbuf + off.k[s] + kt * 32 * ROWB);
       u32x4 t = {w.x, w.y, w.z, w.w};
       sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, t), qf[s],
                                                           sacc[kt], 0, 0, 0);
     }
+}
+
+// Causal mask of a chunk of the diagonal block: key > query is dropped.
+__device__ __forceinline__ void chunk_mask(f32x16 (&sacc)[2], int key0, int qloc, int hi) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (key0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) > qloc) sacc[kt][r] = -INFINITY;
+}
+
+// Chunk max (base 2) of this lane's query, over both key halves.
+__device__ __forceinline__ float chunk_maxval(const f32x16 (&sacc)[2], float sl2) {
   float mblk = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (diag && key0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) > qloc) sacc[kt][r] = -INFINITY;
-      mblk = fmaxf(mblk, sacc[kt][r]);
-    }
-  mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64)) * sl2;
-  const bool raise = mblk > st.m_ref + kRescale;
+    for (int r = 0; r < 16; ++r) mblk = fmaxf(mblk, sacc[kt][r]);
+  return fmaxf(mblk, __shfl_xor(mblk, 32, 64)) * sl2;
+}
+
+// Lazy rescale: when a chunk's max exceeds the reference by more than 8 (base
+// 2), O and l move to the new reference, so every p = 2^(x - m_ref) <= 2^8.
+template <int DT>
+__device__ __forceinline__ void chunk_rescale(SoftmaxState<DT>& st, float mblk, bool valid) {
+  constexpr float kRescale = 8.f;
+  const bool raise = valid && mblk > st.m_ref + kRescale;
   if (__ballot(raise)) {
     const float m_new = raise ? mblk : st.m_ref;
     const float alpha = (st.m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
@@ -169,53 +225,155 @@ __device__ __forceinline__ void prefill_chunk(const uint8_t* kbuf, const uint8_t
       for (int r = 0; r < 16; ++r) st.acc_o[dt][r] *= alpha;
     st.m_ref = m_new;
   }
-  const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
+}
+
+// Slot plan of one pipelined step (NS = 2 D/16 S MFMAs, NP = 4 D/32 P V
+// MFMAs, NT = NS + NP slots, one MFMA per slot):
+//   S(c + 1) keys 0-31 | P V k-steps 0, 1 | S(c + 1) keys 32-63 | P V k-steps 2, 3
+// MFMAs that accumulate into the same registers run back to back where they
+// can (the matrix unit issues such a chain faster than it switches between
+// accumulators): each S half is one chain over the D/16 k-steps, and each P V
+// half goes d-tile by d-tile with its two k-steps together.  The vector work
+// is spread over the slots: P words 0-7 (k-steps 0, 1) over the first S half,
+// words 8-15 over the next S1 slots, each before the first P V MFMA that
+// reads it; the max of the 16 scores of S(c + 1) key half kt (two per unit)
+// follows two slots after that half's last S MFMA.
+template <int D>
+struct StepPlan {
+  static constexpr int DT = D / 32;
+  static constexpr int NS = 2 * (D / 16);
+  static constexpr int NP = 4 * DT;
+  static constexpr int NT = NS + NP;
+  static constexpr int S1 = NS / 2 + NP / 2;   // first slot of the second S half
+  static constexpr int PFD = 2;                // LDS operand reads run this many slots ahead
+  static constexpr bool is_s(int j) { return j < NS / 2 || (j >= S1 && j < S1 + NS / 2); }
+  static constexpr int s_kt(int j) { return j < NS / 2 ? 0 : 1; }
+  static constexpr int s_step(int j) { return j < NS / 2 ? j : j - S1; }
+  static constexpr int pv_local(int j) { return j < S1 ? j - NS / 2 : j - NS; }
+  static constexpr int pv_s(int j) { return 2 * (pv_local(j) / (NP / 2)) + pv_local(j) % 2; }
+  static constexpr int pv_dt(int j) { return (pv_local(j) % (NP / 2)) / 2; }
+  static constexpr int word_slot(int u) { return u < 8 ? u * (NS / 2) / 8 : NS / 2 + (u - 8) * S1 / 8; }
+  static constexpr int max_slot(int kt, int m) {
+    const int start = kt == 0 ? NS / 2 + 1 : S1 + NS / 2 + 1;
+    return start + m * (NT - start) / 8;
+  }
+};
+
+// One pipelined step of a wave, written slot by slot: each slot issues the
+// LDS reads of the MFMA PFD slots ahead, its MFMA, and its share of the vector
+// work; a scheduling fence after each slot keeps that order, so the matrix
+// unit runs while the vector unit works.  P word u is p = 2^(x sl2 - m) for
+// two keys, packed to bf16 for the P V MFMA; the denominator sums the fp32
+// values.  Returns the max (base 2) of S(c + 1) for this lane's query,
+// before any causal mask (the caller masks a diagonal chunk and takes its max
+// again).
+template <int D>
+__device__ __forceinline__ float chunk_step(const uint8_t* kbuf, const uint8_t* vbuf,
+                                            const ChunkOffsets<D>& off, const bf16x8 (&qf)[D / 16],
+                                            const f32x16 (&sacc)[2], f32x16 (&snext)[2],
+                                            SoftmaxState<D / 32>& st, float sl2) {
+  using Plan = StepPlan<D>;
+  constexpr int ROWB = 2 * D;
+  constexpr int DT = Plan::DT, NT = Plan::NT;
+  const float neg_m = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
+  u32x4 pw[4];
+  float lsum = st.l_part;
+  float mx = -INFINITY;
+  auto pword = [&](int u) {
+    const int s = u >> 2, i = u & 3;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * i], sl2, neg_m));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * i + 1], sl2, neg_m));
+    pw[s][i] = cvt_pk_bf16(p0, p1);
+    lsum += p0 + p1;
+  };
+  auto max_unit = [&](int kt, int m) {
+    mx = fmaxf(mx, fmaxf(snext[kt][2 * m], snext[kt][2 * m + 1]));
+  };
+  auto operand = [&](int j) {
+    u32x4 t;
+    if (Plan::is_s(j)) {
+      const uint4 w = *reinterpret_cast<const uint4*>(kbuf + off.k[Plan::s_step(j)] +
+                                                      Plan::s_kt(j) * 32 * ROWB);
+      t = u32x4{w.x, w.y, w.z, w.w};
+    } else {
+      const int s = Plan::pv_s(j), dt = Plan::pv_dt(j);
+      const u32x2 v0 = lds_read_tr(vbuf + off.v[dt][0] + 16 * s * ROWB);
+      const u32x2 v1 = lds_read_tr(vbuf + off.v[dt][1] + 16 * s * ROWB);
+      t = u32x4{v0[0], v0[1], v1[0], v1[1]};
+    }
+    return t;
+  };
+
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sl2, -m_use));
-      sacc[kt][r] = p;
-      st.l_part += p;
+    for (int r = 0; r < 16; ++r) snext[kt][r] = 0.f;
+  constexpr int PFD = Plan::PFD;
+  u32x4 op[NT];
+#pragma unroll
+  for (int j = 0; j < PFD; ++j) op[j] = operand(j);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    if (j + PFD < NT) op[j + PFD] = operand(j + PFD);
+    if (Plan::is_s(j)) {
+      const int kt = Plan::s_kt(j);
+      snext[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, op[j]),
+                                                           qf[Plan::s_step(j)], snext[kt], 0, 0, 0);
+    } else {
+      const int s = Plan::pv_s(j), dt = Plan::pv_dt(j);
+      st.acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, op[j]), __builtin_bit_cast(bf16x8, pw[s]), st.acc_o[dt], 0, 0, 0);
     }
-  // O^T += V^T P^T, 16 keys per k-step.  P^T k-slots 0-3 hold keys 16s + 4hi + i
-  // (registers 8u + i of tile s/2), slots 4-7 keys 16s + 8 + 4hi + i (registers
-  // 8u + 4 + i): registers 8u .. 8u + 7 in order.  The V^T operand (row d = dt*32 +
-  // l32, the same key slots) comes from the transpose read: lane (group G, index i)
-  // addresses key row 16s + 4(G/2) + i/4 [+8] at channels dt*32 + (G%2)*16 + 4(i%4),
-  // and the hardware hands each lane its own column.
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int kt = s >> 1, u = s & 1;
-    u32x4 pw;
+    for (int u = 0; u < 16; ++u)
+      if (Plan::word_slot(u) == j) pword(u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      pw[i] = cvt_pk_bf16(sacc[kt][8 * u + 2 * i], sacc[kt][8 * u + 2 * i + 1]);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-    const int vrow = 16 * s + 4 * (grp16 >> 1) + (i16 >> 2);
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int col = dt * 32 + (grp16 & 1) * 16 + 4 * (i16 & 3);
-      const int chunk = col >> 3, within = (col & 7) * 2;
-      const u32x2 v0 = lds_read_tr(&vbuf[Tile::phys(vrow, chunk) + within]);
-      const u32x2 v1 = lds_read_tr(&vbuf[Tile::phys(vrow + 8, chunk) + within]);
-      u32x4 vw = {v0[0], v0[1], v1[0], v1[1]};
-      st.acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf,
-                                                              st.acc_o[dt], 0, 0, 0);
-    }
+      for (int m = 0; m < 8; ++m)
+        if (Plan::max_slot(kt, m) == j) max_unit(kt, m);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  st.l_part = lsum;
+  return fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
 }
 
+// The slot plan's promises, checked at compile time: every P word is ready
+// before the first P V MFMA that reads it, and each max unit comes at least
+// two slots after the last S MFMA of its key half and inside the step.
+template <int D>
+constexpr bool step_plan_ok() {
+  using Plan = StepPlan<D>;
+  for (int u = 0; u < 16; ++u) {
+    const int s = u / 4;
+    int first = -1;
+    for (int j = 0; j < Plan::NT && first < 0; ++j)
+      if (!Plan::is_s(j) && Plan::pv_s(j) == s) first = j;
+    if (!(Plan::word_slot(u) < first)) return false;
+  }
+  for (int kt = 0; kt < 2; ++kt) {
+    int last = -1;
+    for (int j = 0; j < Plan::NT; ++j)
+      if (Plan::is_s(j) && Plan::s_kt(j) == kt) last = j;
+    for (int m = 0; m < 8; ++m)
+      if (Plan::max_slot(kt, m) < last + 2 || Plan::max_slot(kt, m) >= Plan::NT) return false;
+  }
+  return true;
+}
+static_assert(step_plan_ok<64>() && step_plan_ok<128>(), "prefill step slot plan");
+
 // One work-group per (b, h, I), one wave per 32 queries.  The selected key
-// blocks are walked as 64-key chunks; chunk c's K and V rows live in LDS
-// buffer c % 2 and chunk c + 1 streams into the other buffer (direct-to-LDS,
-// asynchronous) while chunk c is computed, so loads overlap the matrix work.
-// The loop is unrolled by two so each half names its buffers statically.
-// Per chunk each wave computes S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K
-// from LDS, B = Q^T in registers), the online softmax on the accumulators
-// (base 2, scale folded into one FMA, the reference max raised only when a
-// chunk exceeds it by more than 8, so p <= 2^8), and O^T += V^T P^T with P^T
-// taken straight from the S^T registers and V^T from the LDS transpose read.
+// blocks are walked as 64-key chunks.  K runs one chunk ahead of V: while a
+// wave exponentiates chunk c, it already computes S for chunk c + 1, so the
+// matrix unit and the vector unit of a SIMD work at the same time.  LDS holds
+// two K buffers and two V buffers; at the start of step c (one barrier: K(c+1)
+// and V(c) have landed for every wave, and every wave is done with step c - 1)
+// the work-group issues K(c+2) into the K buffer that held K(c) and V(c+1)
+// into the V buffer that held V(c-1), asynchronously (direct-to-LDS), then
+// runs the slot plan above: S(c+1) = K(c+1) Q^T and O += V(c)^T P(c)^T on the
+// matrix unit, P(c) and the max of S(c+1) on the vector unit, followed by the
+// causal mask of a diagonal chunk and the lazy rescale.  The loop is unrolled
+// by two so each half names its buffers statically.
 template <int D, int BS>
 __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -227,9 +385,12 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int CPB = BS / 64;         // 64-key chunks per block
+  // four 64-key tiles.  Separate arrays, not one: the compiler then sees that
+  // the direct-to-LDS loads into one buffer cannot alias the reads of another
+  // and does not wait for them before the reads.
   __shared__ __attribute__((aligned(1024))) uint8_t sK0[Tile::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV0[Tile::BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[Tile::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[Tile::BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[Tile::BYTES];
 
   const int tid = threadIdx.x;
@@ -250,8 +411,10 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
 
   // the block list, read with uniform (scalar) loads; entries out of range or
   // above the diagonal (causal) are skipped
-  const int cnt = blk_cnt[sel0];
-  const int32_t* sel = blk_idx + sel0 * max_sel;
+  // read through the constant address space: the reads are uniform and become
+  // scalar loads, which the vector-load counter the tile waits use does not see
+  const int cnt = ((uniform_i32p)blk_cnt)[sel0];
+  const uniform_i32p sel = (uniform_i32p)(blk_idx + sel0 * max_sel);
   auto next_valid = [&](int from) {
     for (int t = from; t < cnt; ++t) {
       const int J = sel[t];
@@ -259,6 +422,12 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
     return cnt;
   };
+  // chunk cursor: list position t, chunk c within the block (t == cnt: none)
+  auto advance = [&](int& tt, int& cc) {
+    if (tt >= cnt) return;
+    if (cc + 1 < CPB) { ++cc; } else { tt = next_valid(tt + 1); cc = 0; }
+  };
+  auto chunk_row0 = [&](int tt, int cc) { return static_cast<int64_t>(sel[tt]) * BS + cc * 64; };
 
   // Q^T fragments: this lane's query and 8 channels per k-step
   const int qloc = wid * 32 + l32;
@@ -281,46 +450,55 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   st.m_ref = -INFINITY;
   st.l_part = 0.f;
 
-  // chunk cursor: list position t, chunk c within the block
-  int t = next_valid(0), c = 0;
-  auto issue_chunk = [&](int tt, int cc, uint8_t* kb, uint8_t* vb) {
-    const int64_t row0 = static_cast<int64_t>(sel[tt]) * BS + cc * 64;
-    Tile::issue(kbase + row0 * D, kb, wid, lane);
-    Tile::issue(vbase + row0 * D, vb, wid, lane);
-  };
-  auto advance = [&](int& tt, int& cc) {
-    if (cc + 1 < CPB) { ++cc; } else { tt = next_valid(tt + 1); cc = 0; }
-  };
-  // Per chunk: wait for this wave's share of chunk c, barrier (every share has
-  // landed and every wave has finished chunk c - 1, whose buffers are free),
-  // issue chunk c + 1 into those buffers, compute chunk c.
-  if (t < cnt) issue_chunk(t, c, sK0, sV0);
-  while (t < cnt) {
-    // ---- even half: chunk in buffers 0, next chunk into buffers 1
-    {
-      int tn = t, cn = c;
-      advance(tn, cn);
-      wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      if (tn < cnt) issue_chunk(tn, cn, sK1, sV1);
-      const int J = sel[t];
-      prefill_chunk<D>(sK0, sV0, qf, st, sl2, c * 64, qloc, causal && J == I, l32, hi, grp16, i16);
-      t = tn;
-      c = cn;
+  // cursors: (t0, c0) = chunk c (scores in sacc), (t1, c1) = chunk c + 1, (t2, c2) = chunk c + 2
+  int t0 = next_valid(0), c0 = 0;
+  int t1 = t0, c1 = 0;
+  advance(t1, c1);
+  int t2 = t1, c2 = c1;
+  advance(t2, c2);
+
+  ChunkOffsets<D> off;
+  off.init(l32, hi, grp16, i16);
+  f32x16 sacc[2];
+  if (t0 < cnt) {
+    // prologue: K(0) -> K0; then K(1) -> K1 and V(0) -> V0 while S(0) is computed
+    Tile::issue(kbase + chunk_row0(t0, c0) * D, sK0, wid, lane);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (t1 < cnt) Tile::issue(kbase + chunk_row0(t1, c1) * D, sK1, wid, lane);
+    Tile::issue(vbase + chunk_row0(t0, c0) * D, sV0, wid, lane);
+    chunk_scores<D>(sK0, off, qf, sacc);
+    if (causal && sel[t0] == I) chunk_mask(sacc, c0 * 64, qloc, hi);
+    st.m_ref = chunk_maxval(sacc, sl2);  // O and l are still zero: nothing to rescale
+  }
+  // One step: chunk c's P and P V with V in vread, chunk c + 1's S with K in
+  // kread; K(c + 2) goes to kwrite, V(c + 1) to vwrite.  S(c + 1) is computed
+  // even past the last chunk (stale but in-bounds LDS; its max is then
+  // ignored) so that the step body is one straight-line region.
+  auto step = [&](const uint8_t* kread, uint8_t* kwrite, const uint8_t* vread, uint8_t* vwrite) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (t2 < cnt) Tile::issue(kbase + chunk_row0(t2, c2) * D, kwrite, wid, lane);
+    if (t1 < cnt) Tile::issue(vbase + chunk_row0(t1, c1) * D, vwrite, wid, lane);
+    off.pin();
+    const bool next = t1 < cnt;
+    f32x16 snext[2];
+    float mblk = chunk_step<D>(kread, vread, off, qf, sacc, snext, st, sl2);
+    if (causal && next && sel[t1] == I) {  // uniform: chunk c + 1 is on the diagonal
+      chunk_mask(snext, c1 * 64, qloc, hi);
+      mblk = chunk_maxval(snext, sl2);
     }
-    if (t >= cnt) break;
-    // ---- odd half: chunk in buffers 1, next chunk into buffers 0
-    {
-      int tn = t, cn = c;
-      advance(tn, cn);
-      wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      if (tn < cnt) issue_chunk(tn, cn, sK0, sV0);
-      const int J = sel[t];
-      prefill_chunk<D>(sK1, sV1, qf, st, sl2, c * 64, qloc, causal && J == I, l32, hi, grp16, i16);
-      t = tn;
-      c = cn;
-    }
+    chunk_rescale<DT>(st, mblk, next);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) sacc[kt] = snext[kt];
+    t0 = t1; c0 = c1;
+    t1 = t2; c1 = c2;
+    advance(t2, c2);
+  };
+  while (t0 < cnt) {
+    step(sK1, sK0, sV0, sV1);  // c even: K(c+1) in K1, V(c) in V0
+    if (t0 >= cnt) break;
+    step(sK0, sK1, sV1, sV0);  // c odd
   }
 
   // normalise and store: lane holds query qloc, channels dt*32 + 8j + 4hi + i
@@ -360,8 +538,10 @@ __global__ __launch_bounds__(256) void prefill_plain_kernel(
   const int64_t qrow0 = (static_cast<int64_t>(b) * Hq + h) * S;
   const int64_t kvrow0 = (static_cast<int64_t>(b) * Hkv + g) * S;
   const int64_t sel0 = (static_cast<int64_t>(b) * Hq + h) * N + I;
-  const int cnt = blk_cnt[sel0];
-  const int32_t* sel = blk_idx + sel0 * max_sel;
+  // read through the constant address space: the reads are uniform and become
+  // scalar loads, which the vector-load counter the tile waits use does not see
+  const int cnt = ((uniform_i32p)blk_cnt)[sel0];
+  const uniform_i32p sel = (uniform_i32p)(blk_idx + sel0 * max_sel);
 
   for (int qb = 0; qb < block; qb += QPG) {
     const int qi = qb + wid * QPW + lane / LPT;
