@@ -9,7 +9,8 @@
 // channels) is spread over LPT = d/8 lanes with one 16-byte load each, so a
 // wave gathers 4 rows per instruction; the wave first loads its 64 indices
 // with one coalesced load and hands them out by shuffle, then issues all its
-// key and value loads before using any (many bytes in flight per lane).
+// key and value loads together before using any, so a work-group waits for
+// one round of row gathers, with 32 KB in flight per wave.
 // Each work-group leaves (max, sum, unnormalised output) for its split in the
 // workspace; a second kernel merges the splits with the log-sum-exp rule
 //     M = max m_s,  L = sum l_s e^{m_s - M},  o = sum o_s e^{m_s - M} / L.
@@ -61,33 +62,48 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const int first = split * kDecChunk + wid * kDecPerWave;
 
   __shared__ int s_ch[D];
+  __shared__ unsigned long long s_dmask[(D + 63) / 64];
   __shared__ float s_m[kDecWaves], s_l[kDecWaves];
   __shared__ float s_o[kDecWaves][D];
 
-  // channel order of the key row as read by the lanes
+  // this wave's 64 indices, one per lane (issued first: every later load needs them)
+  const int my_pos = first + lane;
+  const int my_idx = (my_pos < cnt) ? tok_idx[static_cast<int64_t>(bh) * max_k + my_pos] : -1;
+
+  // channel order of the key row as the lanes read it: identity, or with the
+  // slab layout the dominant channels (in slab order) followed by the others
+  // in ascending order.  Built in parallel: thread t < D tests channel t
+  // against the dominant set, a ballot gives the set as a bit mask, and a
+  // non-dominant channel's slot is 2 n_dom + the number of non-dominant
+  // channels below it.
   const int dom_w = slab ? 2 * n_dom : D;  // channels stored in `k`
-  if (tid == 0) {
-    if (!slab) {
-      for (int c = 0; c < D; ++c) s_ch[c] = c;
-    } else {
-      uint64_t lo = 0, hi = 0;  // dominant channel set, 128 bits
-      for (int j = 0; j < 2 * n_dom; ++j) {
-        const int ch = dom[g * n_dom + (j % n_dom)] + (j >= n_dom ? P : 0);
-        s_ch[j] = ch;
-        if (ch < 64) lo |= 1ull << ch; else hi |= 1ull << (ch - 64);
-      }
-      int r = 2 * n_dom;
-      for (int c = 0; c < D; ++c) {
-        const bool isdom = c < 64 ? ((lo >> c) & 1ull) : ((hi >> (c - 64)) & 1ull);
-        if (!isdom) s_ch[r++] = c;
+  if (slab) {
+    bool isdom = false;
+    if (tid < D) {
+      for (int j = 0; j < n_dom; ++j) {
+        const int c = dom[g * n_dom + j];
+        isdom |= (tid == c) || (tid == c + P);
       }
     }
+    const unsigned long long m = __ballot(isdom);
+    if (tid < D && lane == 0) s_dmask[wid] = m;
+    // (pairs outside [0, d/2) or repeated give undefined output, never an
+    // access outside the query row or s_ch)
+    if (tid < 2 * n_dom) s_ch[tid] = (dom[g * n_dom + (tid % n_dom)] + (tid >= n_dom ? P : 0)) & (D - 1);
+    __syncthreads();
+    if (tid < D && !isdom) {
+      int below = __popcll(~s_dmask[wid] & ((1ull << lane) - 1ull));
+      if (wid == 1) below += __popcll(~s_dmask[0]);
+      if (2 * n_dom + below < D) s_ch[2 * n_dom + below] = tid;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   float qv[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    qv[j] = Elem<T>::load1(q + static_cast<int64_t>(bh) * D + s_ch[sub * 8 + j]) * scale;
+  for (int j = 0; j < 8; ++j) {
+    const int c = slab ? s_ch[sub * 8 + j] : sub * 8 + j;
+    qv[j] = Elem<T>::load1(q + static_cast<int64_t>(bh) * D + c) * scale;
+  }
 
   const int64_t head_rows = (static_cast<int64_t>(b) * Hkv + g) * Lmax;
   const T* krow_base;
@@ -101,11 +117,6 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     kstride = D - dom_w;
     kofs = sub * 8 - dom_w;
   }
-  const T* vrow_base = v;
-
-  // this wave's 64 indices, one per lane
-  const int my_pos = first + lane;
-  const int my_idx = (my_pos < cnt) ? tok_idx[static_cast<int64_t>(bh) * max_k + my_pos] : -1;
 
   using Raw = typename Elem<T>::Raw;
   int tok[STEPS];
@@ -115,42 +126,37 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     tok[it] = (t >= 0 && t < Lmax) ? t : -1;  // out-of-range entries are ignored
   }
 
-  // phase 1: gather the key rows (all loads in flight), logits
+  // gather every key and value row of the wave before using any of them
+  Raw kr[STEPS], vr[STEPS];
+#pragma unroll
+  for (int it = 0; it < STEPS; ++it) {
+    kr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(krow_base + (head_rows + tok[it]) * kstride + kofs)
+                          : Elem<T>::zero_raw8();
+    vr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(v + (head_rows + tok[it]) * D + sub * 8)
+                          : Elem<T>::zero_raw8();
+  }
   float logit[STEPS];
-  {
-    Raw kr[STEPS];
 #pragma unroll
-    for (int it = 0; it < STEPS; ++it)
-      kr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(krow_base + (head_rows + tok[it]) * kstride + kofs)
-                            : Elem<T>::zero_raw8();
+  for (int it = 0; it < STEPS; ++it) {
+    float kv[8];
+    Elem<T>::unpack8(kr[it], kv);
+    float a = 0.f;
 #pragma unroll
-    for (int it = 0; it < STEPS; ++it) {
-      float kv[8];
-      Elem<T>::unpack8(kr[it], kv);
-      float a = 0.f;
+    for (int j = 0; j < 8; ++j) a = fmaf(qv[j], kv[j], a);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a = fmaf(qv[j], kv[j], a);
-#pragma unroll
-      for (int o = LPT / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, kWave);
-      logit[it] = tok[it] >= 0 ? a : -INFINITY;
-    }
+    for (int o = LPT / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, kWave);
+    logit[it] = tok[it] >= 0 ? a : -INFINITY;
   }
   float mloc = -INFINITY;
 #pragma unroll
   for (int it = 0; it < STEPS; ++it) mloc = fmaxf(mloc, logit[it]);
   const float mw = wave_max(mloc);
 
-  // phase 2: gather the value rows, weighted sum
   float lsum = 0.f;
   float o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = 0.f;
   if (mw > -INFINITY) {
-    Raw vr[STEPS];
-#pragma unroll
-    for (int it = 0; it < STEPS; ++it)
-      vr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(vrow_base + (head_rows + tok[it]) * D + sub * 8)
-                            : Elem<T>::zero_raw8();
 #pragma unroll
     for (int it = 0; it < STEPS; ++it) {
       const float p = tok[it] >= 0 ? __expf(logit[it] - mw) : 0.f;

@@ -100,14 +100,15 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     const int hh = e / NDC, j = e % NDC;
     float v = 0.f;
     if (j < ndc) {
-      const int qc = dom[g * n_dom + (j % n_dom)] + (j >= n_dom ? P : 0);
+      // (a pair outside [0, d/2) gives undefined scores, never a read outside the row)
+      const int qc = (dom[g * n_dom + (j % n_dom)] + (j >= n_dom ? P : 0)) & (d - 1);
       v = Elem<T>::load1(q + (static_cast<int64_t>(b) * Hq + g * GRP + hh) * d + qc) * scale;
     }
     s_q[hh][j] = v;
   }
   if (tid < NDC) {
     int c = 0;
-    if (tid < ndc) c = SLAB ? tid : dom[g * n_dom + (tid % n_dom)] + (tid >= n_dom ? P : 0);
+    if (tid < ndc) c = SLAB ? tid : (dom[g * n_dom + (tid % n_dom)] + (tid >= n_dom ? P : 0)) & (d - 1);
     s_off[tid] = c * ES;  // byte offset of the channel within an unswizzled row
   }
 

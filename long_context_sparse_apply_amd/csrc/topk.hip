@@ -18,12 +18,15 @@
 // a 32-step bitwise search with ballot counts; ties on that key go to the
 // lowest columns through a running count in column order.
 //
-// Long rows (the decode token rows, up to 262144 columns): one 1024-thread
-// work-group per row.  MSB-first radix select on the composite, 11 bits per
-// level with an LDS histogram.  Columns decided at a level are set in an LDS
-// bitmap; once the undecided columns fit in an LDS buffer (4096 entries) the
-// remaining levels run on that buffer, so a row is usually read from memory
-// twice.  The bitmap is finally compacted into ascending column indices.
+// Long rows (the decode token rows, up to 262144 columns): one 512-thread
+// work-group per row.  A sampled threshold (the sample keys' rank that
+// matches k plus a few standard deviations) lets one vectorised pass collect
+// the candidates into an LDS buffer, where an MSB-first radix select (11 bits
+// a level, LDS histogram) marks the k best in an LDS bitmap; an unlucky
+// sample falls back to the radix select reading the row at each level.  The
+// bitmap is finally compacted into ascending column indices.  The LDS is
+// sized per launch from the row length and k, so two rows of the decode
+// workloads share a CU.
 #include "sa_common.hpp"
 
 namespace sa {
@@ -115,13 +118,15 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ long rows
-constexpr int kLongThreads = 1024;
+constexpr int kLongThreads = 512;
 constexpr int kDigit = 11;
 constexpr int kBins = 1 << kDigit;
-constexpr int kCap = 8192;            // LDS candidate buffer (64-bit composites)
-constexpr int kMaxLongCols = 262144;  // LDS bitmap size in columns
+constexpr int kMaxCap = 8192;         // largest LDS candidate buffer (64-bit composites)
+constexpr int kMaxLongCols = 262144;  // longest row (the host rejects longer ones)
 constexpr int kSegs = 64;             // sample segments per row
-constexpr int kSegLen = 128;          // samples per segment (at most)
+constexpr int kSegLen = 256;          // samples per segment (at most)
+constexpr int kCollectVec = 8;        // float4 loads a thread per batch of the collect pass
+constexpr int kSampPerThread = kSegs * kSegLen / kLongThreads;
 
 // exclusive prefix sum over the work-group; returns the prefix, sets total
 __device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& total) {
@@ -159,20 +164,42 @@ __device__ __forceinline__ int comp_col(uint64_t c) {
   return static_cast<int>(0xffffffffu - static_cast<uint32_t>(c & 0xffffffffu));
 }
 
+// Views into the work-group's dynamic LDS: the candidate buffer (cap 64-bit
+// composites), the radix histogram, the selection bitmap (one bit a column)
+// and a few scalars.  Sized per launch from the row length and k.
 struct TopkShared {
-  uint32_t hist[kBins];
-  uint32_t bitmap[kMaxLongCols / 32];
-  uint64_t cbuf[kCap];  // candidate composites; the sample keys live here first
-  int tmp[kLongThreads / kWave];
-  int pick[2];
-  int nbuf;
+  uint64_t* cbuf;
+  uint32_t* hist;
+  uint32_t* bitmap;
+  int* tmp;
+  int* pick;
+  int* nbuf;
+  int cap;
 };
+
+size_t topk_lds_bytes(int cols, int cap) {
+  const size_t words = (static_cast<size_t>(cols) + 31) / 32;
+  return static_cast<size_t>(cap) * 8 + kBins * 4 + words * 4 + (kLongThreads / kWave + 4) * 4;
+}
+
+__device__ __forceinline__ TopkShared topk_views(uint8_t* lds, int cols, int cap) {
+  TopkShared sh;
+  const int words = (cols + 31) / 32;
+  sh.cbuf = reinterpret_cast<uint64_t*>(lds);
+  sh.hist = reinterpret_cast<uint32_t*>(lds + static_cast<size_t>(cap) * 8);
+  sh.bitmap = sh.hist + kBins;
+  sh.tmp = reinterpret_cast<int*>(sh.bitmap + words);
+  sh.pick = sh.tmp + kLongThreads / kWave;
+  sh.nbuf = sh.pick + 2;
+  sh.cap = cap;
+  return sh;
+}
 
 // Histogram level of the MSB-first radix select on 64-bit composites: among
 // the values matching the pbits-bit prefix, find the 11-bit digit b with
 // count(digit > b) < need <= count(digit >= b).  `each` visits every value.
 template <typename Each>
-__device__ __forceinline__ void radix_level(TopkShared& sh, int pbits, uint64_t prefix, int need,
+__device__ __forceinline__ void radix_level(const TopkShared& sh, int pbits, uint64_t prefix, int need,
                                             Each each, int& bsel, int& above, int& cntb) {
   const int tid = threadIdx.x;
   for (int b = tid; b < kBins; b += kLongThreads) sh.hist[b] = 0u;
@@ -207,7 +234,7 @@ __device__ __forceinline__ void radix_level(TopkShared& sh, int pbits, uint64_t 
 
 // Exact selection of the `need` largest composites among cbuf[0, nbuf): marks
 // their columns in the bitmap.
-__device__ void select_in_lds(TopkShared& sh, int nbuf, int need) {
+__device__ void select_in_lds(const TopkShared& sh, int nbuf, int need) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0;
   int pbits = 0;
@@ -237,11 +264,11 @@ __device__ void select_in_lds(TopkShared& sh, int nbuf, int need) {
 
 // Fallback: radix select reading the row from memory at each level, moving
 // to the LDS buffer once the undecided values fit (always exact).
-__device__ void select_from_row(TopkShared& sh, const float* s, int fa, int fb, int need) {
+__device__ void select_from_row(const TopkShared& sh, const float* s, int fa, int fb, int need) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0;
   int pbits = 0;
-  if (tid == 0) sh.nbuf = 0;
+  if (tid == 0) *sh.nbuf = 0;
   __syncthreads();
   while (true) {
     int bsel, above, cntb;
@@ -251,7 +278,7 @@ __device__ void select_from_row(TopkShared& sh, const float* s, int fa, int fb, 
     radix_level(sh, pbits, prefix, need, each, bsel, above, cntb);
     need -= above;
     const bool done = (cntb == need);
-    const bool collect = !done && cntb <= kCap;
+    const bool collect = !done && cntb <= sh.cap;
     for (int i = fa + tid; i < fb; i += kLongThreads) {
       const uint64_t c = composite(order_key(s[i]), i);
       if (pbits != 0 && (c >> (64 - pbits)) != prefix) continue;
@@ -259,13 +286,13 @@ __device__ void select_from_row(TopkShared& sh, const float* s, int fa, int fb, 
       if (dg > bsel || (done && dg == bsel)) {
         atomicOr(&sh.bitmap[i >> 5], 1u << (i & 31));
       } else if (collect && dg == bsel) {
-        sh.cbuf[atomicAdd(&sh.nbuf, 1)] = c;
+        sh.cbuf[atomicAdd(sh.nbuf, 1)] = c;
       }
     }
     __syncthreads();
     if (done) return;
     if (collect) {
-      const int nb = sh.nbuf;
+      const int nb = *sh.nbuf;
       // keep only the collected values: the prefix now covers pbits + 11 bits
       select_in_lds(sh, nb, need);
       return;
@@ -275,31 +302,43 @@ __device__ void select_from_row(TopkShared& sh, const float* s, int fa, int fb, 
   }
 }
 
-// wave-aggregated append of `c` (where pred) to the candidate buffer
-__device__ __forceinline__ void append(TopkShared& sh, bool pred, uint64_t c) {
-  const uint64_t m = __ballot(pred);
-  if (m == 0) return;
+// Wave-aggregated append of up to four composites a lane (where ok[e]) to the
+// candidate buffer: one LDS atomic per wave for all of them.
+__device__ __forceinline__ void append4(const TopkShared& sh, const bool (&ok)[4], const uint64_t (&c)[4]) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int leader = __ffsll(static_cast<long long>(m)) - 1;
+  uint64_t m[4];
+  int tot = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m[e] = __ballot(ok[e]);
+    tot += __popcll(m[e]);
+  }
+  if (tot == 0) return;
+  const int leader = __ffsll(static_cast<long long>(m[0] | m[1] | m[2] | m[3])) - 1;
   int base = 0;
-  if (lane == leader) base = atomicAdd(&sh.nbuf, __popcll(m));
+  if (lane == leader) base = atomicAdd(sh.nbuf, tot);
   base = __shfl(base, leader, kWave);
-  if (pred) {
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    const int pos = base + __popcll(m & below);
-    if (pos < kCap) sh.cbuf[pos] = c;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (ok[e]) {
+      const int pos = base + __popcll(m[e] & below);
+      if (pos < sh.cap) sh.cbuf[pos] = c[e];
+    }
+    base += __popcll(m[e]);
   }
 }
 
-// One 1024-thread work-group per row.
+// One 512-thread work-group per row.
 //  1. Samples: kSegs contiguous segments spread over the candidate columns
-//     (about 1/16 of them); the threshold t_low is the sample key of rank
-//     k * (samples / candidates) plus four standard deviations plus 8, so that
-//     with high probability at least k candidates, and not many more, have a
-//     key >= t_low.
-//  2. One vectorised pass appends every candidate with key >= t_low (as a
-//     64-bit composite) to the LDS buffer.
-//  3. If the count is in [k, kCap], an exact radix select in LDS marks the k
+//     (up to 16384 values, read once and kept in registers); the
+//     threshold t_low is the sample key of rank k * (samples / candidates)
+//     plus four standard deviations plus 8, so that with high probability at
+//     least k candidates, and not many more, have a key >= t_low.
+//  2. One vectorised, software-pipelined pass (two batches of 8 float4 loads
+//     a thread) appends every candidate with key >= t_low (as a 64-bit
+//     composite) to the LDS buffer.
+//  3. If the count is in [k, cap], an exact radix select in LDS marks the k
 //     best; otherwise (an unlucky sample) the exact row-reading radix select
 //     runs instead.  Either way the result is exact.
 //  4. The bitmap (forced + selected columns) is compacted into ascending
@@ -307,10 +346,10 @@ __device__ __forceinline__ void append(TopkShared& sh, bool pred, uint64_t c) {
 __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
     const float* __restrict__ scores, int cols, const int32_t* __restrict__ valid_len,
     const int32_t* __restrict__ k_per_row, int k_const, int n_sink, int n_local,
-    int32_t* __restrict__ idx_out, int max_out, int32_t* __restrict__ count_out) {
-  __shared__ TopkShared sh;
+    int32_t* __restrict__ idx_out, int max_out, int32_t* __restrict__ count_out, int cap) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t topk_lds[];
+  const TopkShared sh = topk_views(topk_lds, cols, cap);
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
   const int64_t row = blockIdx.x;
   int n, k;
   row_params(row, cols, valid_len, k_per_row, k_const, n, k);
@@ -321,7 +360,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
   const int ncand = fb - fa;
 
   for (int w = tid; w < nwords; w += kLongThreads) sh.bitmap[w] = 0u;
-  if (tid == 0) sh.nbuf = 0;
+  if (tid == 0) *sh.nbuf = 0;
   __syncthreads();
   for (int i = tid; i < fa; i += kLongThreads) atomicOr(&sh.bitmap[i >> 5], 1u << (i & 31));
   for (int i = fb + tid; i < n; i += kLongThreads) atomicOr(&sh.bitmap[i >> 5], 1u << (i & 31));
@@ -335,80 +374,103 @@ __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
     const double expect = static_cast<double>(k) * nsamp / ncand;
     int rank = static_cast<int>(expect + 4.0 * sqrt(expect) + 8.0);
     if (nsamp >= 1024 && rank < nsamp) {
-      // 1. sample keys -> cbuf as composites (sample index as tie-break)
-      uint32_t* samp = reinterpret_cast<uint32_t*>(sh.cbuf);
+      // 1. the rank-th largest sample (sample index as tie-break); each thread
+      //    keeps its samples' keys in registers for the radix levels
       const int seg_stride = ncand / kSegs;
-      for (int e = tid; e < nsamp; e += kLongThreads) {
-        const int seg = e / seg_len, o = e % seg_len;
-        samp[e] = order_key(s[fa + seg * seg_stride + o]);
+      uint32_t skey[kSampPerThread];
+#pragma unroll
+      for (int j = 0; j < kSampPerThread; ++j) {
+        const int e = tid + j * kLongThreads;
+        skey[j] = e < nsamp ? order_key(s[fa + (e / seg_len) * seg_stride + e % seg_len]) : 0u;
       }
-      __syncthreads();
-      // widen in place to composites (backwards: the u64 slots overlap the u32 ones)
-      for (int base = ((nsamp - 1) / kLongThreads) * kLongThreads; base >= 0; base -= kLongThreads) {
-        const int e = base + tid;
-        uint32_t kv = 0;
-        if (e < nsamp) kv = samp[e];
-        __syncthreads();
-        if (e < nsamp) sh.cbuf[e] = composite(kv, e);
-        __syncthreads();
-      }
-      // the rank-th largest sample
       uint64_t prefix = 0;
       int pbits = 0, need = rank;
       while (true) {
         int bsel, above, cntb;
         auto each = [&](auto f) {
-          for (int i = tid; i < nsamp; i += kLongThreads) f(sh.cbuf[i]);
+#pragma unroll
+          for (int j = 0; j < kSampPerThread; ++j) {
+            const int e = tid + j * kLongThreads;
+            if (e < nsamp) f(composite(skey[j], e));
+          }
         };
         radix_level(sh, pbits, prefix, need, each, bsel, above, cntb);
         need -= above;
         prefix = (prefix << kDigit) | static_cast<uint64_t>(bsel);
         pbits += kDigit;
-        if (cntb == 1 || pbits >= 33) break;  // the key (top 32 bits) is decided by then
+        // 22 key bits (sign, exponent and 13 mantissa bits) place the
+        // threshold within about 1e-4 of the sample at that rank: enough
+        if (cntb == 1 || pbits >= 22) break;
       }
-      // top 32 bits of the prefix = the sample key at that rank (or a prefix of it)
+      // the key prefix, low bits zero: at most the sample key at that rank
       const uint32_t t_low = pbits >= 32 ? static_cast<uint32_t>(prefix >> (pbits - 32))
                                           : static_cast<uint32_t>(prefix << (32 - pbits));
       __syncthreads();
-      if (tid == 0) sh.nbuf = 0;
+      if (tid == 0) *sh.nbuf = 0;
       __syncthreads();
-      // 2. collect every candidate with key >= t_low
+      // 2. collect every candidate with key >= t_low.  For a value that is not
+      //    NaN, key(v) >= t_low is v >= f_low, f_low the float whose key is
+      //    t_low; a t_low at or below the key of -inf takes every value (NaN
+      //    ranks as -inf), one above the key of +inf gives a NaN f_low that
+      //    no value passes.
+      const bool take_all = t_low <= 0x007fffffu;
+      const float f_low = (t_low & 0x80000000u) ? __uint_as_float(t_low & 0x7fffffffu)
+                                                : __uint_as_float(~t_low);
+      auto qualifies = [&](float v) { return take_all || v >= f_low; };
       const bool aligned = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
       const int a0 = aligned ? ((fa + 3) & ~3) : fb;
       const int a1 = aligned ? (fb & ~3) : fb;
       for (int i = fa + tid; i < (a0 < fb ? a0 : fb); i += kLongThreads) {
-        const uint32_t kv = order_key(s[i]);
-        if (kv >= t_low) append(sh, true, composite(kv, i));
+        const float v = s[i];
+        const bool ok[4] = {qualifies(v), false, false, false};
+        const uint64_t c[4] = {composite(order_key(v), i), 0, 0, 0};
+        append4(sh, ok, c);
       }
-      for (int base = a0; base < a1; base += 4 * kLongThreads * 4) {
-        float4 v4[4];
-        int i4[4];
+      // vectorised body, software-pipelined: the next batch of float4 loads is
+      // in flight while the current one is tested
+      constexpr int kStep = 4 * kLongThreads * kCollectVec;
+      float4 cur[kCollectVec];
+      auto load_batch = [&](float4 (&dst)[kCollectVec], int base) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          i4[u] = base + (u * kLongThreads + tid) * 4;
-          v4[u] = i4[u] < a1 ? *reinterpret_cast<const float4*>(s + i4[u])
-                             : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        for (int u = 0; u < kCollectVec; ++u) {
+          const int i = base + (u * kLongThreads + tid) * 4;
+          dst[u] = i < a1 ? *reinterpret_cast<const float4*>(s + i)
+                          : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }
+      };
+      if (a0 < a1) load_batch(cur, a0);
+      for (int base = a0; base < a1; base += kStep) {
+        float4 nxt[kCollectVec];
+        if (base + kStep < a1) load_batch(nxt, base + kStep);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float vv[4] = {v4[u].x, v4[u].y, v4[u].z, v4[u].w};
+        for (int u = 0; u < kCollectVec; ++u) {
+          const int i = base + (u * kLongThreads + tid) * 4;
+          const float vv[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+          bool ok[4];
+          bool any = false;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t kv = order_key(vv[e]);
-            const bool ok = i4[u] < a1 && kv >= t_low;
-            append(sh, ok, composite(kv, i4[u] + e));
+            ok[e] = i < a1 && qualifies(vv[e]);
+            any |= ok[e];
           }
+          if (__ballot(any) == 0) continue;  // the common case: nothing here qualifies
+          const uint64_t c[4] = {composite(order_key(vv[0]), i), composite(order_key(vv[1]), i + 1),
+                                 composite(order_key(vv[2]), i + 2), composite(order_key(vv[3]), i + 3)};
+          append4(sh, ok, c);
         }
+#pragma unroll
+        for (int u = 0; u < kCollectVec; ++u) cur[u] = nxt[u];
       }
       for (int i = (a1 > a0 ? a1 : a0) + tid; i < fb; i += kLongThreads) {
-        const uint32_t kv = order_key(s[i]);
-        if (kv >= t_low) append(sh, true, composite(kv, i));
+        const float v = s[i];
+        const bool ok[4] = {qualifies(v), false, false, false};
+        const uint64_t c[4] = {composite(order_key(v), i), 0, 0, 0};
+        append4(sh, ok, c);
       }
-      (void)lane;
       __syncthreads();
-      const int got = sh.nbuf;
+      const int got = *sh.nbuf;
       __syncthreads();
-      if (got >= k && got <= kCap) {
+      if (got >= k && got <= cap) {
         select_in_lds(sh, got, k);
         done = true;
       }
@@ -452,8 +514,19 @@ hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_
     else SA_TOPK_W(16);
 #undef SA_TOPK_W
   } else {
-    topk_block_kernel<<<dim3(static_cast<unsigned>(rows)), kLongThreads, 0, st>>>(
-        scores, cols, valid_len, k_per_row, k_const, n_sink, n_local, idx_out, max_out, count_out);
+    // candidate buffer: k plus a quarter plus 1024 (the sampled threshold
+    // overshoots k by a few standard deviations), at most kMaxCap
+    int cap = k_const + k_const / 4 + 1024;
+    cap = ((cap + 63) / 64) * 64;
+    if (cap > kMaxCap) cap = kMaxCap;
+    const size_t lds = topk_lds_bytes(cols, cap);
+    // allow the largest size this kernel ever asks for (above the 64 KB default)
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_block_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(topk_lds_bytes(kMaxLongCols, kMaxCap)));
+    if (e != hipSuccess) return e;
+    topk_block_kernel<<<dim3(static_cast<unsigned>(rows)), kLongThreads, lds, st>>>(
+        scores, cols, valid_len, k_per_row, k_const, n_sink, n_local, idx_out, max_out, count_out, cap);
   }
   return hipGetLastError();
 }
