@@ -123,6 +123,19 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Max / sum of a value over lanes l and l ^ 32 (the two key halves of a
+// query) with v_permlane32_swap, which trades the wave's 32-lane halves
+// without an LDS round trip: for lane l < 32 the pair is (x[l], x[l + 32]),
+// for lane l >= 32 it is (x[l - 32], x[l]).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
@@ -206,7 +219,7 @@ __device__ __forceinline__ float chunk_maxval(const f32x16 (&sacc)[2], float sl2
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mblk = fmaxf(mblk, sacc[kt][r]);
-  return fmaxf(mblk, __shfl_xor(mblk, 32, 64)) * sl2;
+  return pair_max(mblk) * sl2;
 }
 
 // Lazy rescale: when a chunk's max exceeds the reference by more than 8 (base
@@ -335,7 +348,7 @@ __device__ __forceinline__ float chunk_step(const uint8_t* kbuf, const uint8_t* 
     __builtin_amdgcn_sched_barrier(0);
   }
   st.l_part = lsum;
-  return fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+  return pair_max(mx) * sl2;
 }
 
 // The slot plan's promises, checked at compile time: every P word is ready
@@ -502,7 +515,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 
   // normalise and store: lane holds query qloc, channels dt*32 + 8j + 4hi + i
-  const float l_run = st.l_part + __shfl_xor(st.l_part, 32, 64);
+  const float l_run = pair_sum(st.l_part);
   const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
   uint16_t* op = out + (qrow0 + qloc) * D;
 #pragma unroll
