@@ -4,15 +4,19 @@
 // attention over the selected subset T_t, at the tokens' original positions)
 // and sec. 2.C (both variants read only the selected key/value rows).
 //
-// Grid: (splits, B*Hq).  A work-group takes 256 consecutive entries of one
-// (b, h) selection list; each of its 4 waves takes 64.  A token row (d
-// channels) is spread over LPT = d/8 lanes with one 16-byte load each, so a
-// wave gathers 4 rows per instruction; the wave first loads its 64 indices
-// with one coalesced load and hands them out by shuffle, then issues all its
-// key and value loads together before using any, so a work-group waits for
-// one round of row gathers, with 32 KB in flight per wave.
-// Each work-group leaves (max, sum, unnormalised output) for its split in the
-// workspace; a second kernel merges the splits with the log-sum-exp rule
+// Grid: (splits, B*Hq).  A work-group walks cpw chunks of 256 consecutive
+// entries of one (b, h) selection list; each of its 4 waves takes 64 entries
+// of a chunk and keeps a running softmax over its chunks.  With at least two
+// lists per CU a work-group takes a whole list (cpw = all chunks, one pass);
+// with fewer, each takes one chunk and a merge pass combines the splits.
+// A token row (d channels) is spread over LPT = d/8 lanes with one 16-byte
+// load each, so a wave gathers 4 rows per instruction; for each chunk the
+// wave first loads its 64 indices with one coalesced load and hands them out
+// by shuffle, then issues all its key and value loads together before using
+// any (32 KB in flight per wave).
+// A one-pass work-group writes the output itself; otherwise each leaves
+// (max, sum, unnormalised output) for its split in the workspace and a
+// second kernel merges the splits with the log-sum-exp rule
 //     M = max m_s,  L = sum l_s e^{m_s - M},  o = sum o_s e^{m_s - M} / L.
 //
 // With the dominant-slab key layout the key row is the concatenation of its
@@ -26,6 +30,7 @@ namespace sa {
 constexpr int kDecChunk = 256;
 constexpr int kDecWaves = 4;
 constexpr int kDecPerWave = kDecChunk / kDecWaves;
+constexpr int kChipCUs = 256;  // MI355X compute units
 
 int decode_splits(int max_k) {
   const int s = (max_k + kDecChunk - 1) / kDecChunk;
@@ -42,8 +47,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ k_rest,
     const T* __restrict__ v, int Hq, int Hkv, int Lmax, const int32_t* __restrict__ dom,
     int n_dom, int slab, const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ tok_cnt,
-    int max_k, float scale, int splits, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    float* __restrict__ ws_o) {
+    int max_k, float scale, int splits, int cpw, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    float* __restrict__ ws_o, T* __restrict__ out, float* __restrict__ lse) {
   constexpr int LPT = D / 8;
   constexpr int TPI = kWave / LPT;
   constexpr int STEPS = kDecPerWave / TPI;
@@ -59,16 +64,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const int b = bh / Hq;
   const int g = h / (Hq / Hkv);
   const int cnt = tok_cnt[bh];
-  const int first = split * kDecChunk + wid * kDecPerWave;
 
   __shared__ int s_ch[D];
   __shared__ unsigned long long s_dmask[(D + 63) / 64];
   __shared__ float s_m[kDecWaves], s_l[kDecWaves];
   __shared__ float s_o[kDecWaves][D];
-
-  // this wave's 64 indices, one per lane (issued first: every later load needs them)
-  const int my_pos = first + lane;
-  const int my_idx = (my_pos < cnt) ? tok_idx[static_cast<int64_t>(bh) * max_k + my_pos] : -1;
 
   // channel order of the key row as the lanes read it: identity, or with the
   // slab layout the dominant channels (in slab order) followed by the others
@@ -119,54 +119,67 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   }
 
   using Raw = typename Elem<T>::Raw;
-  int tok[STEPS];
-#pragma unroll
-  for (int it = 0; it < STEPS; ++it) {
-    const int t = __shfl(my_idx, it * TPI + grp_tok, kWave);
-    tok[it] = (t >= 0 && t < Lmax) ? t : -1;  // out-of-range entries are ignored
-  }
-
-  // gather every key and value row of the wave before using any of them
-  Raw kr[STEPS], vr[STEPS];
-#pragma unroll
-  for (int it = 0; it < STEPS; ++it) {
-    kr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(krow_base + (head_rows + tok[it]) * kstride + kofs)
-                          : Elem<T>::zero_raw8();
-    vr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(v + (head_rows + tok[it]) * D + sub * 8)
-                          : Elem<T>::zero_raw8();
-  }
-  float logit[STEPS];
-#pragma unroll
-  for (int it = 0; it < STEPS; ++it) {
-    float kv[8];
-    Elem<T>::unpack8(kr[it], kv);
-    float a = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) a = fmaf(qv[j], kv[j], a);
-#pragma unroll
-    for (int o = LPT / 2; o >= 1; o >>= 1) a += __shfl_xor(a, o, kWave);
-    logit[it] = tok[it] >= 0 ? a : -INFINITY;
-  }
-  float mloc = -INFINITY;
-#pragma unroll
-  for (int it = 0; it < STEPS; ++it) mloc = fmaxf(mloc, logit[it]);
-  const float mw = wave_max(mloc);
-
-  float lsum = 0.f;
+  // running softmax state of this wave over its share of cpw chunks
+  float m_run = -INFINITY, lsum = 0.f;
   float o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = 0.f;
-  if (mw > -INFINITY) {
+  for (int ci = 0; ci < cpw; ++ci) {
+    const int first = (split * cpw + ci) * kDecChunk + wid * kDecPerWave;
+    if (first >= cnt) break;
+    // this wave's 64 indices, one per lane (every later load needs them)
+    const int my_pos = first + lane;
+    const int my_idx = (my_pos < cnt) ? tok_idx[static_cast<int64_t>(bh) * max_k + my_pos] : -1;
+    int tok[STEPS];
 #pragma unroll
     for (int it = 0; it < STEPS; ++it) {
-      const float p = tok[it] >= 0 ? __expf(logit[it] - mw) : 0.f;
-      lsum += p;
-      float vv[8];
-      Elem<T>::unpack8(vr[it], vv);
+      const int t = __shfl(my_idx, it * TPI + grp_tok, kWave);
+      tok[it] = (t >= 0 && t < Lmax) ? t : -1;  // out-of-range entries are ignored
+    }
+    // gather every key and value row of the wave before using any of them
+    Raw kr[STEPS], vr[STEPS];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = fmaf(p, vv[j], o[j]);
+    for (int it = 0; it < STEPS; ++it) {
+      kr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(krow_base + (head_rows + tok[it]) * kstride + kofs)
+                            : Elem<T>::zero_raw8();
+      vr[it] = tok[it] >= 0 ? Elem<T>::load_raw8(v + (head_rows + tok[it]) * D + sub * 8)
+                            : Elem<T>::zero_raw8();
+    }
+    float logit[STEPS];
+#pragma unroll
+    for (int it = 0; it < STEPS; ++it) {
+      float kv[8];
+      Elem<T>::unpack8(kr[it], kv);
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a = fmaf(qv[j], kv[j], a);
+#pragma unroll
+      for (int sh = LPT / 2; sh >= 1; sh >>= 1) a += __shfl_xor(a, sh, kWave);
+      logit[it] = tok[it] >= 0 ? a : -INFINITY;
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < STEPS; ++it) mloc = fmaxf(mloc, logit[it]);
+    const float mw = wave_max(mloc);
+    if (mw > -INFINITY) {
+      const float m_new = fmaxf(m_run, mw);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int it = 0; it < STEPS; ++it) {
+        const float p = tok[it] >= 0 ? __expf(logit[it] - m_run) : 0.f;
+        lsum += p;
+        float vv[8];
+        Elem<T>::unpack8(vr[it], vv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = fmaf(p, vv[j], o[j]);
+      }
     }
   }
+  const float mw = m_run;
 #pragma unroll
   for (int off = LPT; off < kWave; off <<= 1) {
     lsum += __shfl_xor(lsum, off, kWave);
@@ -182,7 +195,6 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     for (int j = 0; j < 8; ++j) s_o[wid][lane * 8 + j] = o[j];
   }
   __syncthreads();
-  const int64_t part = static_cast<int64_t>(bh) * splits + split;
   if (tid < D) {
     float M = -INFINITY;
 #pragma unroll
@@ -196,10 +208,17 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         O += s_o[w][tid] * f;
       }
     }
-    ws_o[part * D + tid] = O;
-    if (tid == 0) {
-      ws_m[part] = M;
-      ws_l[part] = L;
+    if (splits == 1) {
+      // the work-group saw every selected token: final output, no merge pass
+      Elem<T>::store1(out + static_cast<int64_t>(bh) * D + tid, (L > 0.f) ? O / L : 0.f);
+      if (lse && tid == 0) lse[bh] = (L > 0.f) ? M + logf(L) : -INFINITY;
+    } else {
+      const int64_t part = static_cast<int64_t>(bh) * splits + split;
+      ws_o[part * D + tid] = O;
+      if (tid == 0) {
+        ws_m[part] = M;
+        ws_l[part] = L;
+      }
     }
   }
 }
@@ -235,7 +254,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* k_rest, const
                          const int32_t* tok_idx, const int32_t* tok_cnt, int max_k, float scale,
                          void* out, float* lse, void* ws, hipStream_t st) {
   (void)cache_len;
-  const int splits = decode_splits(max_k);
+  // With at least two (b, h) rows per CU of the chip a work-group takes a
+  // whole selection list (one pass, no merge); otherwise each takes 256
+  // entries and a merge pass combines the splits.
+  const int nchunks = decode_splits(max_k);
+  const int rows = B * Hq;
+  const int cpw = rows >= 2 * kChipCUs ? nchunks : 1;
+  const int splits = (nchunks + cpw - 1) / cpw;
   const int64_t parts = static_cast<int64_t>(B) * Hq * splits;
   float* ws_m = static_cast<float*>(ws);
   float* ws_l = ws_m + parts;
@@ -245,9 +270,10 @@ hipError_t launch_decode(const void* q, const void* k, const void* k_rest, const
   decode_partial_kernel<T, D><<<grid, 256, 0, st>>>(                                              \
       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(k_rest),          \
       static_cast<const T*>(v), Hq, Hkv, Lmax, dom, n_dom, slab, tok_idx, tok_cnt, max_k, scale,  \
-      splits, ws_m, ws_l, ws_o);                                                                  \
-  decode_merge_kernel<T, D><<<dim3(B * Hq), D, 0, st>>>(ws_m, ws_l, ws_o, splits,                 \
-                                                        static_cast<T*>(out), lse)
+      splits, cpw, ws_m, ws_l, ws_o, static_cast<T*>(out), lse);                                  \
+  if (splits > 1)                                                                                 \
+    decode_merge_kernel<T, D><<<dim3(B * Hq), D, 0, st>>>(ws_m, ws_l, ws_o, splits,               \
+                                                          static_cast<T*>(out), lse)
   if (dtype == kBF16) {
     if (d == 128) { SA_DEC(uint16_t, 128); } else { SA_DEC(uint16_t, 64); }
   } else {
