@@ -59,13 +59,44 @@ def decode_bytes(tok_cnt, d, elem=2):
     return float(tok_cnt.sum()) * 2 * d * elem
 
 
-def time_prefill(layer, steps, warmup, torch):
+def decode_dedup_bytes(tok_idx, tok_cnt, hkv, d, elem=2):
+    """K and V bytes if each KV head's rows were gathered once for its query heads:
+    the union of the selections of the query heads that share a KV head."""
+    B, Hq, _ = tok_idx.shape
+    grp = Hq // hkv
+    rows = 0
+    for b in range(B):
+        for g in range(hkv):
+            sel = [tok_idx[b, h, :tok_cnt[b, h]] for h in range(g * grp, (g + 1) * grp)]
+            rows += np.unique(np.concatenate(sel)).size
+    return float(rows) * 2 * d * elem
+
+
+class CacheFlush:
+    """Fills a 1 GiB buffer before each timed step, so L2 and the MALL hold
+    nothing from the previous iteration (the fill itself is not timed)."""
+
+    def __init__(self, torch, enabled=True):
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if enabled else None
+
+    def __call__(self):
+        if self.buf is not None:
+            self.buf.zero_()
+
+
+def _stats(x):
+    x = np.asarray(x, dtype=np.float64)
+    return float(np.median(x)), float(np.percentile(x, 10)), float(np.percentile(x, 90))
+
+
+def time_prefill(layer, steps, warmup, torch, flush):
     for _ in range(warmup):
         layer.run()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
+        flush()
         e = ev[i]
         e[0].record()
         layer.score()
@@ -77,19 +108,21 @@ def time_prefill(layer, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])  # ms
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
-    return dict(step_ms=float(np.mean(step_ms)), wall_ms=wall * 1e3,
-                score_ms=float(parts[:, 0].mean()), select_ms=float(parts[:, 1].mean()),
-                attend_ms=float(parts[:, 2].mean()), attend_ms_p10=float(np.percentile(parts[:, 2], 10)),
-                attend_ms_p90=float(np.percentile(parts[:, 2], 90)))
+    step = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    r = dict(wall_ms=wall * 1e3, attend_ms_mean=float(parts[:, 2].mean()))
+    for name, col in (("step_ms", step), ("score_ms", parts[:, 0]), ("select_ms", parts[:, 1]),
+                      ("attend_ms", parts[:, 2])):
+        r[name], r[name + "_p10"], r[name + "_p90"] = _stats(col)
+    return r
 
 
-def time_decode(step, steps, warmup, torch):
+def time_decode(step, steps, warmup, torch, flush):
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for i in range(steps):
+        flush()
         e = ev[i]
         e[0].record()
         step.rope()
@@ -101,14 +134,36 @@ def time_decode(step, steps, warmup, torch):
         step.attend()
         e[4].record()
     torch.cuda.synchronize()
-    parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
-    total = np.array([e[0].elapsed_time(e[4]) for e in ev])
-    return dict(step_us=float(total.mean() * 1e3), rope_us=float(parts[:, 0].mean() * 1e3),
-                score_us=float(parts[:, 1].mean() * 1e3), select_us=float(parts[:, 2].mean() * 1e3),
-                attend_us=float(parts[:, 3].mean() * 1e3))
+    parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev]) * 1e3
+    total = np.array([e[0].elapsed_time(e[4]) for e in ev]) * 1e3
+    r = dict(attend_us_mean=float(parts[:, 3].mean()))
+    for name, col in (("step_us", total), ("rope_us", parts[:, 0]), ("score_us", parts[:, 1]),
+                      ("select_us", parts[:, 2]), ("attend_us", parts[:, 3])):
+        r[name], r[name + "_p10"], r[name + "_p90"] = _stats(col)
+    return r
 
 
-def run_prefill(cfg, steps, warmup, torch):
+def copy_reference(torch, reps=5):
+    """Achieved GB/s of a 1 GiB device-to-device copy (1 GiB read + 1 GiB
+    written), timed in the same run as a practical HBM reference."""
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9
+
+
+def run_prefill(cfg, steps, warmup, torch, flush):
     import synth.device as SD
     from long_context_sparse_apply_amd.pipeline import PrefillLayer
     q, k, v = SD.prefill_tensors(cfg)
@@ -116,7 +171,7 @@ def run_prefill(cfg, steps, warmup, torch):
                          band_split_pair=cfg.band_split_pair, n_sink=cfg.n_sink,
                          n_local=cfg.n_local, keep_const=cfg.keep_const,
                          keep_percent=cfg.keep_percent)
-    t = time_prefill(layer, steps, warmup, torch)
+    t = time_prefill(layer, steps, warmup, torch, flush)
     fl, tile_fl = prefill_flops(layer.blk_idx.cpu().numpy(), layer.blk_cnt.cpu().numpy(),
                                 cfg.block, cfg.d)
     t["attend_tflops"] = fl / (t["attend_ms"] * 1e-3) / 1e12
@@ -132,16 +187,19 @@ def run_prefill(cfg, steps, warmup, torch):
     return t
 
 
-def run_decode(cfg, steps, warmup, torch):
+def run_decode(cfg, steps, warmup, torch, flush):
     import synth.device as SD
     from long_context_sparse_apply_amd.pipeline import DecodeStep
     dt = SD.decode_tensors(cfg)
     step = DecodeStep(dt["q_raw"], dt["k"], dt["v"], dt["lens"], dt["dom"], theta=cfg.theta,
                       top_k=cfg.k, slab=bool(cfg.slab), k_rest=dt["k_rest"])
-    t = time_decode(step, steps, warmup, torch)
-    gb = decode_bytes(step.tok_cnt.cpu().numpy(), cfg.d)
+    t = time_decode(step, steps, warmup, torch, flush)
+    cnt = step.tok_cnt.cpu().numpy()
+    gb = decode_bytes(cnt, cfg.d)
     t["attend_gather_bytes"] = gb
     t["attend_hbm_frac"] = gb / (t["attend_us"] * 1e-6) / PEAK_HBM_BPS
+    t["attend_gather_bytes_dedup_per_kv_head"] = decode_dedup_bytes(step.tok_idx.cpu().numpy(), cnt,
+                                                                    cfg.Hkv, cfg.d)
     row = 2 * cfg.n_dom if cfg.slab else cfg.d
     scan = float(cfg.B) * cfg.Hkv * cfg.L * row * 2 + float(cfg.B) * cfg.Hq * cfg.L * 4
     t["score_bytes"] = scan
@@ -199,6 +257,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="C2|C3|C4|C5: run one workload (profiling)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not clear L2 / MALL with a 1 GiB fill before each timed step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first copy 1 GiB device-to-device 3 times (a kernel of known bytes "
                          "that scales the HBM traffic counters)")
@@ -221,41 +281,51 @@ def main():
         log("copied 1 GiB x3")
         del src, dst
         torch.cuda.empty_cache()
+    flush = CacheFlush(torch, enabled=not args.no_flush)
     if args.only:
         cfg = W.CONFIGS[args.only]
         log(f"running {args.only} only")
-        r = run_prefill(cfg, args.steps, args.warmup, torch) if args.only in ("C2", "C3") \
-            else run_decode(cfg, args.steps, args.warmup, torch)
+        r = run_prefill(cfg, args.steps, args.warmup, torch, flush) if args.only in ("C2", "C3") \
+            else run_decode(cfg, args.steps, args.warmup, torch, flush)
         log(json.dumps(r))
         return
 
+    copy_gbps = copy_reference(torch)
+    log(f"1 GiB device copy: {copy_gbps:.0f} GB/s")
     cfg = W.C2
     log("C2: prefill 32K")
-    main_r = run_prefill(cfg, args.steps, args.warmup, torch)
+    main_r = run_prefill(cfg, args.steps, args.warmup, torch, flush)
     log(json.dumps(main_r))
     secondary = {}
     if not args.no_secondary:
         log("C3: prefill 128K")
-        r3 = run_prefill(W.C3, max(3, args.steps // 4), 2, torch)
+        r3 = run_prefill(W.C3, max(3, args.steps // 4), 2, torch, flush)
         log(json.dumps(r3))
         secondary["prefill_128k"] = {"tok_per_s": r3["tok_per_s"], "ms_per_step": r3["step_ms"],
+                                     "ms_per_step_p10_p90": [r3["step_ms_p10"], r3["step_ms_p90"]],
                                      "attend_ms": r3["attend_ms"],
                                      "attend_mfma_frac": r3["attend_mfma_frac"],
                                      "score_ms": r3["score_ms"], "select_ms": r3["select_ms"]}
         for name, c in (("decode_64k", W.C4), ("decode_128k_slab", W.C5)):
             log(f"{name}")
-            rd = run_decode(c, args.steps, args.warmup, torch)
+            rd = run_decode(c, args.steps, args.warmup, torch, flush)
             log(json.dumps(rd))
-            secondary[name] = {"us_per_step": rd["step_us"], "rope_us": rd["rope_us"],
-                               "score_us": rd["score_us"], "select_us": rd["select_us"],
-                               "attend_us": rd["attend_us"],
+            secondary[name] = {"us_per_step": rd["step_us"],
+                               "us_per_step_p10_p90": [rd["step_us_p10"], rd["step_us_p90"]],
+                               "rope_us": rd["rope_us"], "score_us": rd["score_us"],
+                               "select_us": rd["select_us"], "attend_us": rd["attend_us"],
                                "attend_hbm_frac": rd["attend_hbm_frac"],
+                               "attend_gather_bytes": rd["attend_gather_bytes"],
+                               "attend_gather_bytes_dedup_per_kv_head":
+                                   rd["attend_gather_bytes_dedup_per_kv_head"],
                                "score_hbm_frac": rd["score_hbm_frac"]}
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(cfg)
-    achieved = main_r["attend_flops"] / (main_r["attend_ms"] * 1e-3) / 1e12
+    # the roofline uses the attention kernel's mean launch duration (as a
+    # kernel trace reports it); the step figures are medians
+    achieved = main_r["attend_flops"] / (main_r["attend_ms_mean"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": main_r["tok_per_s"],
@@ -277,11 +347,16 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved * 1e12 / PEAK_BF16_FLOPS,
                      "traffic": measured_traffic(TRAFFIC_SUMMARY, PREFILL_SOURCE),
                      "kernel": "prefill_mfma_kernel",
-                     "avg_launch_ms": main_r["attend_ms"],
+                     "avg_launch_ms": main_r["attend_ms_mean"],
                      "flops_per_launch": main_r["attend_flops"],
                      "tile_flops_per_launch": main_r["attend_tile_flops"]},
+        "ms_per_step_p10_p90": [main_r["step_ms_p10"], main_r["step_ms_p90"]],
         "stages_ms": {"score": main_r["score_ms"], "select": main_r["select_ms"],
                       "attend": main_r["attend_ms"]},
+        "timing": ("HIP events on the kernels' stream; medians of the timed steps; L2 and MALL "
+                   "cleared by a 1 GiB fill before each step" if not args.no_flush else
+                   "HIP events on the kernels' stream; medians of the timed steps; no cache flush"),
+        "hbm_reference": {"copy_GBps": copy_gbps, "peak_GBps": PEAK_HBM_BPS / 1e9},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
