@@ -73,15 +73,22 @@ def decode_dedup_bytes(tok_idx, tok_cnt, hkv, d, elem=2):
 
 
 class CacheFlush:
-    """Fills a 1 GiB buffer before each timed step, so L2 and the MALL hold
-    nothing from the previous iteration (the fill itself is not timed)."""
+    """Reads a 1 GiB buffer before each timed step, so L2 and the MALL hold
+    nothing from the previous iteration.  A read sweep, not a fill: the
+    previous step's dirty lines are written back during the sweep, and the
+    sweep leaves no dirty lines of its own to be written back inside the
+    timed step.  Not timed."""
 
     def __init__(self, torch, enabled=True):
-        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if enabled else None
+        self.buf = None
+        self.torch = torch
+        if enabled:
+            self.buf = torch.zeros(1 << 27, dtype=torch.int64, device="cuda")  # 1 GiB
+            self.out = torch.empty((), dtype=torch.int64, device="cuda")
 
     def __call__(self):
         if self.buf is not None:
-            self.buf.zero_()
+            self.torch.amax(self.buf, dim=0, out=self.out)
 
 
 def _stats(x):
@@ -141,6 +148,67 @@ def time_decode(step, steps, warmup, torch, flush):
                       ("select_us", parts[:, 2]), ("attend_us", parts[:, 3])):
         r[name], r[name + "_p10"], r[name + "_p90"] = _stats(col)
     return r
+
+
+def time_call(fn, steps, warmup, torch, flush):
+    """Median / p10 / p90 (us) of one enqueued call, HIP events around it."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return _stats(np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3)
+
+
+def run_cache_append(cfg_p, cfg_d, steps, warmup, torch, flush):
+    """sa_kv_cache_append at its two uses: the prefill -> decode handoff (the
+    whole prompt's keys rotated and values copied into a decode cache) and one
+    decode token per batch row.  Algorithmic bytes: raw K and V read once,
+    rotated K and V written once."""
+    import synth
+    import synth.device as SD
+    from long_context_sparse_apply_amd import sa_kv_cache_append
+    from synth import workloads as W
+    dev = "cuda"
+    q, k, v = SD.prefill_tensors(cfg_p)
+    del q
+    dom = torch.from_numpy(W.dominant_pairs(cfg_d)).to(dev)
+    n = dom.shape[1]
+    out = {}
+
+    def one(name, k_new, v_new, Lmax, start_row):
+        B, Hkv, S, d = k_new.shape
+        start = torch.full((B,), start_row, dtype=torch.int32, device=dev)
+        for slab in (False, True):
+            kc = torch.zeros((B, Hkv, Lmax, 2 * n if slab else d), dtype=k_new.dtype, device=dev)
+            kr = (torch.zeros((B, Hkv, Lmax, d - 2 * n), dtype=k_new.dtype, device=dev)
+                  if slab else None)
+            vc = torch.zeros((B, Hkv, Lmax, d), dtype=k_new.dtype, device=dev)
+
+            def fn():
+                sa_kv_cache_append(k_new, v_new, start, kc, vc, theta=cfg_p.theta, k_rest=kr,
+                                   dom_pairs=dom if slab else None, slab=slab)
+            med, p10, p90 = time_call(fn, steps, warmup, torch, flush)
+            nbytes = 4.0 * k_new.numel() * k_new.element_size()
+            key = f"{name}_{'slab' if slab else 'std'}"
+            out[key] = {"us": med, "us_p10_p90": [p10, p90], "bytes": nbytes,
+                        "hbm_frac": nbytes / (med * 1e-6) / PEAK_HBM_BPS}
+            del kc, kr, vc
+    one("prompt_32k", k, v, cfg_p.S, 0)
+    del k, v
+    kt = torch.empty((cfg_d.B, cfg_d.Hkv, 1, cfg_d.d), dtype=torch.bfloat16, device=dev)
+    vt = torch.empty_like(kt)
+    SD.fill(kt, cfg_d.seed, synth.TID_K)
+    SD.fill(vt, cfg_d.seed, synth.TID_V)
+    one("token_b64", kt, vt, 4096, 4000)
+    torch.cuda.empty_cache()
+    return out
 
 
 def copy_reference(torch, reps=5):
@@ -258,7 +326,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="C2|C3|C4|C5: run one workload (profiling)")
     ap.add_argument("--no-flush", action="store_true",
-                    help="do not clear L2 / MALL with a 1 GiB fill before each timed step")
+                    help="do not clear L2 / MALL with a 1 GiB read sweep before each timed step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first copy 1 GiB device-to-device 3 times (a kernel of known bytes "
                          "that scales the HBM traffic counters)")
@@ -319,6 +387,10 @@ def main():
                                "attend_gather_bytes_dedup_per_kv_head":
                                    rd["attend_gather_bytes_dedup_per_kv_head"],
                                "score_hbm_frac": rd["score_hbm_frac"]}
+        log("cache append (prefill -> decode handoff, decode token)")
+        ra = run_cache_append(cfg, W.C5, args.steps, args.warmup, torch, flush)
+        log(json.dumps(ra))
+        secondary["cache_append"] = ra
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -354,7 +426,7 @@ def main():
         "stages_ms": {"score": main_r["score_ms"], "select": main_r["select_ms"],
                       "attend": main_r["attend_ms"]},
         "timing": ("HIP events on the kernels' stream; medians of the timed steps; L2 and MALL "
-                   "cleared by a 1 GiB fill before each step" if not args.no_flush else
+                   "cleared by a 1 GiB read sweep before each step" if not args.no_flush else
                    "HIP events on the kernels' stream; medians of the timed steps; no cache flush"),
         "hbm_reference": {"copy_GBps": copy_gbps, "peak_GBps": PEAK_HBM_BPS / 1e9},
         "cpu_baseline": cpu,

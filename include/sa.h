@@ -70,6 +70,36 @@ sa_status sa_rope_apply(const void* x, void* out, sa_dtype dtype, int B, int H, 
                         const int32_t* pos, int pos0, double theta, void* stream);
 
 /*
+ * sa_kv_cache_append -- write S new tokens into a decode KV cache: keys
+ * rotated at their absolute positions, values as they are.  FASA sec. 2.B
+ * item 2 (attention over the selected tokens keeps their original absolute
+ * positions, so the cache holds keys rotated at those positions) and
+ * sec. 2.C (the computation-optimised variant scores from the dominant
+ * channels, kept together in a slab).  Used to hand a prefilled prompt to
+ * decode (S = prompt length, start = 0) and to append each decoded token
+ * (S = 1, start = current cache length).
+ *   k_new, v_new : [B, Hkv, S, d] dtype, raw (not rotated) keys and values.
+ *   start : device int32 [B]: token s of batch b goes to cache row (and
+ *           position) start[b] + s; rows outside [0, Lmax) are skipped.
+ *   slab == 0: k_cache [B, Hkv, Lmax, d].
+ *   slab == 1: k_cache = k_dom [B, Hkv, Lmax, 2*n_dom] and k_rest
+ *           [B, Hkv, Lmax, d - 2*n_dom], laid out as in sa_token_score
+ *           (dom_pairs [Hkv, n_dom], distinct pairs < d/2).
+ *   v_cache [B, Hkv, Lmax, d].
+ * The angle p * omega_i is formed and reduced modulo 2*pi in fp64, the
+ * rotation is applied in fp32, then stored in dtype (as sa_rope_apply).
+ * Only the written rows change.  Entries of start / dom_pairs are not checked
+ * on the host; out-of-range values give undefined cache contents, never a
+ * write outside the cache.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE (B, Hkv, S, Lmax < 1 or d not 64/128),
+ *         SA_ERR_RANGE (theta <= 1, n_dom outside [1, d/2]), SA_ERR_DTYPE.
+ */
+sa_status sa_kv_cache_append(const void* k_new, const void* v_new, sa_dtype dtype, int B,
+                             int Hkv, int S, int d, int Lmax, const int32_t* start, double theta,
+                             int slab, const int32_t* dom_pairs, int n_dom, void* k_cache,
+                             void* k_rest, void* v_cache, void* stream);
+
+/*
  * sa_block_score -- Prism block importance estimation for prefill.
  * Prism sec. 1 (block importance from mean-pooled block vectors), sec. 3
  * item 1 (dual-band pooling), sec. 3 item 2 (energy-based temperature

@@ -22,9 +22,9 @@ SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_RANGE, SA_ERR_WORKSPACE, 
 SA_F32, SA_BF16 = 0, 1
 SA_OP_BLOCK_SCORE, SA_OP_TOPK, SA_OP_DECODE = 1, 2, 3
 
-EXPORTED = ("sa_rope_apply", "sa_block_score", "sa_token_score", "sa_topk_select",
-            "sa_sparse_attn_prefill", "sa_sparse_attn_decode", "sa_workspace_bytes",
-            "sa_status_string", "sa_version")
+EXPORTED = ("sa_rope_apply", "sa_kv_cache_append", "sa_block_score", "sa_token_score",
+            "sa_topk_select", "sa_sparse_attn_prefill", "sa_sparse_attn_decode",
+            "sa_workspace_bytes", "sa_status_string", "sa_version")
 
 
 class SAError(RuntimeError):
@@ -41,6 +41,7 @@ def _load() -> ctypes.CDLL:
                            ctypes.c_float, ctypes.c_size_t)
     sig = {
         "sa_rope_apply": [P, P, I, I, I, I, I, P, I, D, P],
+        "sa_kv_cache_append": [P, P, I, I, I, I, I, I, P, D, I, P, I, P, P, P, P],
         "sa_block_score": [P, P, I, I, I, I, I, I, D, I, I, I, F, I, P, P, P, P, P, P, SZ, P],
         "sa_token_score": [P, P, P, I, I, I, I, I, I, P, P, I, I, F, P, P],
         "sa_topk_select": [P, I64, I, P, P, I, I, I, P, I, P, P, SZ, P],
@@ -127,6 +128,46 @@ def sa_rope_apply(x, out, theta: float, pos=None, pos0: int = 0, stream=None):
     _call("sa_rope_apply", _ptr(x), _ptr(out), _dtype_code(x), B, H, S, d, _ptr(pos), pos0,
           float(theta), _stream(stream))
     return out
+
+
+def sa_kv_cache_append(k_new, v_new, start, k_cache, v_cache, *, theta: float, k_rest=None,
+                       dom_pairs=None, slab: bool = False, stream=None):
+    """Write new tokens into a decode KV cache.
+
+    k_new, v_new: [B, Hkv, S, d] raw keys and values; start: int32 [B], the
+    cache row (= absolute position) of each batch's first new token.
+    slab False: k_cache [B, Hkv, Lmax, d].  slab True: k_cache = k_dom
+    [B, Hkv, Lmax, 2*n_dom], k_rest [B, Hkv, Lmax, d - 2*n_dom], dom_pairs
+    int32 [Hkv, n_dom].  v_cache [B, Hkv, Lmax, d].
+    """
+    torch = _torch()
+    _check(k_new, "k_new", ndim=4)
+    _check(v_new, "v_new", k_new.dtype, 4)
+    _check(start, "start", torch.int32, 1)
+    _check(k_cache, "k_cache", k_new.dtype, 4)
+    _check(k_rest, "k_rest", k_new.dtype, 4)
+    _check(v_cache, "v_cache", k_new.dtype, 4)
+    _check(dom_pairs, "dom_pairs", torch.int32, 2)
+    B, Hkv, S, d = k_new.shape
+    if tuple(v_new.shape) != (B, Hkv, S, d) or start.shape[0] != B:
+        raise ValueError("k_new / v_new / start shapes disagree")
+    Lmax = v_cache.shape[2]
+    if tuple(v_cache.shape) != (B, Hkv, Lmax, d):
+        raise ValueError("v_cache must be [B, Hkv, Lmax, d]")
+    n_dom = 0
+    if slab:
+        if dom_pairs is None:
+            raise ValueError("slab layout needs dom_pairs")
+        n_dom = dom_pairs.shape[1]
+        if tuple(k_cache.shape) != (B, Hkv, Lmax, 2 * n_dom):
+            raise ValueError("k_dom must be [B, Hkv, Lmax, 2*n_dom]")
+        if k_rest is not None and tuple(k_rest.shape) != (B, Hkv, Lmax, d - 2 * n_dom):
+            raise ValueError("k_rest must be [B, Hkv, Lmax, d - 2*n_dom]")
+    elif tuple(k_cache.shape) != (B, Hkv, Lmax, d):
+        raise ValueError("k_cache must be [B, Hkv, Lmax, d]")
+    _call("sa_kv_cache_append", _ptr(k_new), _ptr(v_new), _dtype_code(k_new), B, Hkv, S, d, Lmax,
+          _ptr(start), float(theta), int(bool(slab)), _ptr(dom_pairs), n_dom, _ptr(k_cache),
+          _ptr(k_rest), _ptr(v_cache), _stream(stream))
 
 
 def sa_block_score(q, k, scores, *, theta: float, block: int, band_split_pair: int,

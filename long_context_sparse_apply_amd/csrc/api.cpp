@@ -35,6 +35,25 @@ sa_status sa_rope_apply(const void* x, void* out, sa_dtype dtype, int B, int H, 
   return launched(sa::launch_rope(x, out, dtype, B, H, S, d, pos, pos0, fr, as_stream(stream)));
 }
 
+sa_status sa_kv_cache_append(const void* k_new, const void* v_new, sa_dtype dtype, int B,
+                             int Hkv, int S, int d, int Lmax, const int32_t* start, double theta,
+                             int slab, const int32_t* dom_pairs, int n_dom, void* k_cache,
+                             void* k_rest, void* v_cache, void* stream) {
+  if (!dtype_ok(dtype)) return SA_ERR_DTYPE;
+  if (!k_new || !v_new || !start || !k_cache || !v_cache) return SA_ERR_NULL;
+  if (B < 1 || Hkv < 1 || S < 1 || Lmax < 1 || !head_dim_ok(d)) return SA_ERR_SHAPE;
+  if (!(theta > 1.0)) return SA_ERR_RANGE;
+  if (slab) {
+    if (!dom_pairs) return SA_ERR_NULL;
+    if (n_dom < 1 || 2 * n_dom > d) return SA_ERR_RANGE;
+    if (2 * n_dom < d && !k_rest) return SA_ERR_NULL;
+  }
+  const sa::RopeFreq fr = sa::make_rope_freq(d, theta);
+  return launched(sa::launch_kv_append(k_new, v_new, dtype, B, Hkv, S, d, Lmax, start, fr,
+                                       slab ? 1 : 0, dom_pairs, slab ? n_dom : 0, k_cache, k_rest,
+                                       v_cache, as_stream(stream)));
+}
+
 sa_status sa_block_score(const void* q, const void* k, sa_dtype dtype, int B, int Hq, int Hkv,
                          int S, int d, double theta, int block, int band_split_pair,
                          int calibrate, float sm_scale, int causal, void* q_rope_out,

@@ -24,6 +24,13 @@ enum { kF32 = 0, kBF16 = 1 };
 hipError_t launch_rope(const void* x, void* out, int dtype, int B, int H, int S, int d,
                        const int32_t* pos, int pos0, const RopeFreq& fr, hipStream_t st);
 
+// rotate new keys at their cache positions and write them (standard or slab
+// layout) with their values into the decode cache
+hipError_t launch_kv_append(const void* k_new, const void* v_new, int dtype, int B, int Hkv,
+                            int S, int d, int Lmax, const int32_t* start, const RopeFreq& fr,
+                            int slab, const int32_t* dom, int n_dom, void* k_out, void* k_rest,
+                            void* v_out, hipStream_t st);
+
 // fused rotation + calibrated dual-band block pooling of Q and K (one pass)
 hipError_t launch_rope_pool(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int S,
                             int d, int block, int split, int calibrate, const RopeFreq& fr,

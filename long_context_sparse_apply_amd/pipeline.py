@@ -8,6 +8,8 @@ Prefill ("Prism: Spectral-Aware Block-Sparse Attention"):
     sa_topk_select  -> per query block: sink + local + top-k blocks
     sa_sparse_attn_prefill -> attention over the selected blocks
 Decode ("FASA: Frequency-aware Sparse Attention"):
+    sa_kv_cache_append -> the new token's key rotated at its position, written
+                      with its value into the cache (standard or dominant slab)
     sa_rope_apply   -> the decode query rotated at position L_b - 1
     sa_token_score  -> dominant-chunk token scores
     sa_topk_select  -> top-k tokens
@@ -18,8 +20,8 @@ from __future__ import annotations
 import torch
 
 from . import (SA_OP_BLOCK_SCORE, SA_OP_DECODE, prefill_row_params, sa_block_score,
-               sa_rope_apply, sa_sparse_attn_decode, sa_sparse_attn_prefill, sa_token_score,
-               sa_topk_select, workspace_bytes)
+               sa_kv_cache_append, sa_rope_apply, sa_sparse_attn_decode, sa_sparse_attn_prefill,
+               sa_token_score, sa_topk_select, workspace_bytes)
 
 
 class PrefillLayer:
@@ -78,6 +80,45 @@ class PrefillLayer:
         self.select()
         self.attend()
         return self.out
+
+
+class DecodeCache:
+    """A decode KV cache of ``Lmax`` rows per (batch, KV head) plus its lengths.
+
+    Keys are stored rotated at their absolute positions (the row index), in
+    the standard layout ``k [B, Hkv, Lmax, d]`` or, with ``slab``, as the
+    dominant slab ``k [B, Hkv, Lmax, 2*n_dom]`` plus ``k_rest [B, Hkv, Lmax,
+    d - 2*n_dom]``.  ``lens`` (int32 [B], on the device) counts the rows
+    written so far; appends go to row ``lens[b]`` onward.
+    """
+
+    def __init__(self, B, Hkv, Lmax, d, *, dtype, device, theta, dom_pairs, slab=False):
+        self.B, self.Hkv, self.Lmax, self.d = B, Hkv, Lmax, d
+        self.theta, self.slab, self.dom = theta, slab, dom_pairs
+        n_dom = dom_pairs.shape[1]
+        kd = 2 * n_dom if slab else d
+        self.k = torch.zeros((B, Hkv, Lmax, kd), dtype=dtype, device=device)
+        self.k_rest = (torch.zeros((B, Hkv, Lmax, d - kd), dtype=dtype, device=device)
+                       if slab and kd < d else None)
+        self.v = torch.zeros((B, Hkv, Lmax, d), dtype=dtype, device=device)
+        self.lens = torch.zeros(B, dtype=torch.int32, device=device)
+
+    def append(self, k_new, v_new, batch=None):
+        """Append ``S`` raw tokens ``[B, Hkv, S, d]`` to every batch row, or
+        ``[1, Hkv, S, d]`` to batch row ``batch`` alone.  Rows past ``Lmax``
+        are dropped and not counted."""
+        S = k_new.shape[2]
+        sl = slice(None) if batch is None else slice(batch, batch + 1)
+        k_rest = None if self.k_rest is None else self.k_rest[sl]
+        lens = self.lens[sl]
+        sa_kv_cache_append(k_new, v_new, lens, self.k[sl], self.v[sl], theta=self.theta,
+                           k_rest=k_rest, dom_pairs=self.dom, slab=self.slab)
+        lens.add_(S).clamp_(max=self.Lmax)
+
+    def step(self, q_raw, *, top_k, sm_scale=None):
+        """A decode step for the query ``q_raw [B, Hq, d]`` of the newest token."""
+        return DecodeStep(q_raw, self.k, self.v, self.lens, self.dom, theta=self.theta,
+                          top_k=top_k, slab=self.slab, k_rest=self.k_rest, sm_scale=sm_scale)
 
 
 class DecodeStep:

@@ -8,6 +8,10 @@
   scores: the worst kept candidate is not clearly worse than the best dropped
   one (each side widened by the score tolerance), and the count is right.
 * Attention outputs: within 2e-2 absolute for bf16 storage, 1e-5 for fp32.
+* Rotated cache rows (:func:`rotated_bounds`): the GPU rotates in fp32 with
+  an fp64-reduced angle, so each value lies within 2^-20 (|x_i| + |x_{i+P}|)
+  of the oracle's fp64 rotation; stored as bf16 it must be one of the
+  roundings of that interval (one value except next to a rounding midpoint).
 """
 from __future__ import annotations
 
@@ -18,6 +22,22 @@ import numpy as np
 SCORE_RTOL = 1e-4
 GAP_RTOL = 1e-3
 OUT_ATOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+ROT_ERR = 2.0 ** -20
+
+
+def rotated_bounds(ref: np.ndarray, x_raw: np.ndarray, dtype: str):
+    """Admissible [lo, hi] for the stored GPU rotation of ``x_raw`` given the
+    oracle's fp64 rotation ``ref`` (same shape, last axis d)."""
+    from synth import round_to_bf16
+    P = x_raw.shape[-1] // 2
+    pair = np.abs(x_raw[..., :P]).astype(np.float64) + np.abs(x_raw[..., P:])
+    e = ROT_ERR * np.concatenate([pair, pair], axis=-1) + 2.0 ** -23 * np.abs(ref)
+    lo, hi = ref - e, ref + e
+    if dtype == "bf16":
+        return (round_to_bf16(lo).astype(np.float64), round_to_bf16(hi).astype(np.float64))
+    return lo, hi
 
 
 def say(msg: str):

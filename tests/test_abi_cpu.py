@@ -51,6 +51,22 @@ def test_validation_errors_before_launch():
     assert L.sa_rope_apply(P(), P(), 1, 1, 1, 8, 96, None, 0, 1e4, None) == sa.SA_ERR_SHAPE
     assert L.sa_rope_apply(P(), P(), 1, 1, 1, 8, 128, None, 0, 1.0, None) == sa.SA_ERR_RANGE
     assert L.sa_rope_apply(P(), P(), 7, 1, 1, 8, 128, None, 0, 1e4, None) == sa.SA_ERR_DTYPE
+    # kv cache append: null pointers, shapes, theta, slab rules
+    def kva(kn=True, start=True, B=2, Hkv=2, S=4, d=128, Lmax=64, theta=1e4, slab=0, dom=None,
+            n_dom=16, rest=None, dtype=1):
+        return L.sa_kv_cache_append(P() if kn else None, P(), dtype, B, Hkv, S, d, Lmax,
+                                    P() if start else None, theta, slab, dom, n_dom, P(), rest, P(),
+                                    None)
+    assert kva(kn=False) == sa.SA_ERR_NULL
+    assert kva(start=False) == sa.SA_ERR_NULL
+    assert kva(S=0) == sa.SA_ERR_SHAPE
+    assert kva(Lmax=0) == sa.SA_ERR_SHAPE
+    assert kva(d=96) == sa.SA_ERR_SHAPE
+    assert kva(theta=0.5) == sa.SA_ERR_RANGE
+    assert kva(dtype=5) == sa.SA_ERR_DTYPE
+    assert kva(slab=1) == sa.SA_ERR_NULL                      # no dominant pairs
+    assert kva(slab=1, dom=P(), n_dom=65) == sa.SA_ERR_RANGE
+    assert kva(slab=1, dom=P(), n_dom=16) == sa.SA_ERR_NULL   # no k_rest while 2*n_dom < d
     # block score: S % block, Hq % Hkv, split range, workspace
     args = dict(theta=1e4, block=64, split=16)
     def bs(B=1, Hq=4, Hkv=2, S=512, d=64, block=64, split=16, ws=None, wsb=0, pq=None, pk=None):
