@@ -68,9 +68,12 @@ __device__ __forceinline__ void prefill_work_item(int x, int nwg, int B, int Hq,
 //  - a V transpose read (8 bytes a lane, 4 aligned rows x 2 or 4 adjacent
 //    chunks) does too, since bits 1-2 and bits 2-3 of sw are one-to-one on
 //    (a0, a1).
-// Tiles are filled by direct-to-LDS loads (global_load_lds_dwordx4): one wave
-// instruction writes 1 KB of consecutive LDS bytes, lane i its 16 bytes at
-// offset 16 i, and each lane fetches the global chunk that belongs there.
+// Tiles are filled by direct-to-LDS loads (buffer_load_dwordx4 ... lds): one
+// wave instruction writes 1 KB of consecutive LDS bytes, lane i its 16 bytes
+// at offset 16 i, and each lane fetches the global chunk that belongs there.
+// The buffer form, not the global one: while a global-form load to LDS is in
+// flight the compiler waits for every outstanding LDS read before each use,
+// which would undo the operand reads the step plan issues ahead.
 template <int D, int ROWS, int NW>
 struct LdsTile {
   static constexpr int ROWB = D * 2;                 // bytes per row
@@ -89,6 +92,7 @@ struct LdsTile {
   }
   // issue this wave's share of the tile's direct-to-LDS loads (asynchronous)
   static __device__ __forceinline__ void issue(const uint16_t* g, uint8_t* lds, int wid, int lane) {
+    const auto rsrc = buffer_rsrc(g, BYTES);
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int ins = wid * LPW + j;
@@ -96,8 +100,7 @@ struct LdsTile {
       const int row = off / ROWB;
       const int pos = (off % ROWB) >> 4;
       const int chunk = pos ^ sw(row);
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(g) + row * ROWB + chunk * 16;
-      lds_dma16(src, lds + ins * 1024);
+      lds_dma16_buf(rsrc, row * ROWB + chunk * 16, lds + ins * 1024);
     }
   }
 };

@@ -104,6 +104,23 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) 
   __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
 }
 
+// The same through a buffer resource (buffer_load_dwordx4 ... lds): lane i
+// fetches base + voffset and writes lds_wave_base + 16 i; offsets at or past
+// `bytes` read zeros.  The compiler keeps exact counts for LDS reads issued
+// while such a load is in flight (with the global form above it waits for
+// all of them before any use), so a wave can keep several operand reads in
+// flight across the tile loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  // dword 3 = 0x00020000: raw (untyped) 32-bit buffer access on this family
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, int voffset,
+                                              void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, voffset, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
