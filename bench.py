@@ -166,6 +166,37 @@ def time_call(fn, steps, warmup, torch, flush):
     return _stats(np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3)
 
 
+def run_decode_host_rest(cfg, steps, warmup, torch, flush):
+    """FASA-M placement (memory-optimised variant): the dominant slab and the
+    scores in device memory; the non-dominant key channels and the values in
+    pinned host memory.  Scoring reads the slab only; the attention reads the
+    selected rows of k_rest and v over the host link.  Host-link bytes per
+    step = selected (b, h, token) x (rest-of-key + value row bytes)."""
+    import synth.device as SD
+    from long_context_sparse_apply_amd.pipeline import DecodeStep
+    dt = SD.decode_tensors(cfg)
+    k_rest = torch.empty(dt["k_rest"].shape, dtype=dt["k_rest"].dtype, pin_memory=True)
+    v = torch.empty(dt["v"].shape, dtype=dt["v"].dtype, pin_memory=True)
+    k_rest.copy_(dt["k_rest"])
+    v.copy_(dt["v"])
+    torch.cuda.synchronize()
+    del dt["k_rest"], dt["v"]
+    torch.cuda.empty_cache()
+    step = DecodeStep(dt["q_raw"], dt["k"], v, dt["lens"], dt["dom"], theta=cfg.theta,
+                      top_k=cfg.k, slab=True, k_rest=k_rest)
+    t = time_decode(step, steps, warmup, torch, flush)
+    cnt = step.tok_cnt.cpu().numpy()
+    row_host = (cfg.d - 2 * cfg.n_dom) * 2 + cfg.d * 2
+    host_bytes = float(cnt.sum()) * row_host
+    t["host_link_bytes"] = host_bytes
+    t["host_link_GBps"] = host_bytes / (t["attend_us"] * 1e-6) / 1e9
+    t["device_resident_bytes"] = float(dt["k"].numel() * 2)
+    t["host_resident_bytes"] = float((k_rest.numel() + v.numel()) * 2)
+    del step, dt, k_rest, v
+    torch.cuda.empty_cache()
+    return t
+
+
 def run_cache_append(cfg_p, cfg_d, steps, warmup, torch, flush):
     """sa_kv_cache_append at its two uses: the prefill -> decode handoff (the
     whole prompt's keys rotated and values copied into a decode cache) and one
@@ -387,6 +418,18 @@ def main():
                                "attend_gather_bytes_dedup_per_kv_head":
                                    rd["attend_gather_bytes_dedup_per_kv_head"],
                                "score_hbm_frac": rd["score_hbm_frac"]}
+        log("decode_64k_slab_host_rest (FASA-M placement)")
+        cfg_m = W.C5.with_(B=16, L=65536, k=2048)
+        rm = run_decode_host_rest(cfg_m, max(2, args.steps // 5), 1, torch, flush)
+        log(json.dumps(rm))
+        secondary["decode_64k_slab_host_rest"] = {
+            "workload": "batch 16, KV length 65536, dominant slab (16 pairs) in HBM, "
+                        "rest of K and V in pinned host memory, top-2048, bf16",
+            "us_per_step": rm["step_us"], "score_us": rm["score_us"],
+            "select_us": rm["select_us"], "attend_us": rm["attend_us"],
+            "host_link_bytes": rm["host_link_bytes"], "host_link_GBps": rm["host_link_GBps"],
+            "device_resident_bytes": rm["device_resident_bytes"],
+            "host_resident_bytes": rm["host_resident_bytes"]}
         log("cache append (prefill -> decode handoff, decode token)")
         ra = run_cache_append(cfg, W.C5, args.steps, args.warmup, torch, flush)
         log(json.dumps(ra))

@@ -26,6 +26,12 @@
  *  - Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
  *  - The library keeps no mutable global state; distinct streams may call it
  *    concurrently with distinct buffers.
+ *  - Host placement (FASA sec. 2.C, the memory-optimised variant FASA-M):
+ *    where an entry point says so, a buffer may instead be pinned host memory
+ *    allocated with hipHostMalloc (or a framework's pinned allocator built on
+ *    it).  The library looks up its device mapping with
+ *    hipPointerGetAttributes and the kernels reach it over the host link;
+ *    host memory the device cannot reach (pageable) returns SA_ERR_ACCESS.
  */
 #ifndef SA_H
 #define SA_H
@@ -45,7 +51,9 @@ typedef enum {
   SA_ERR_RANGE = 4,       /* a parameter outside its documented range           */
   SA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required         */
   SA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement        */
-  SA_ERR_HIP = 7          /* a HIP launch or runtime call failed                */
+  SA_ERR_HIP = 7,         /* a HIP launch or runtime call failed                */
+  SA_ERR_ACCESS = 8       /* a buffer the device cannot read or write (pageable
+                             host memory where pinned memory is allowed)        */
 } sa_status;
 
 typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
@@ -85,14 +93,16 @@ sa_status sa_rope_apply(const void* x, void* out, sa_dtype dtype, int B, int H, 
  *   slab == 1: k_cache = k_dom [B, Hkv, Lmax, 2*n_dom] and k_rest
  *           [B, Hkv, Lmax, d - 2*n_dom], laid out as in sa_token_score
  *           (dom_pairs [Hkv, n_dom], distinct pairs < d/2).
- *   v_cache [B, Hkv, Lmax, d].
+ *   v_cache [B, Hkv, Lmax, d].  k_rest and v_cache may be pinned host memory
+ *           (host placement, FASA-M).
  * The angle p * omega_i is formed and reduced modulo 2*pi in fp64, the
  * rotation is applied in fp32, then stored in dtype (as sa_rope_apply).
  * Only the written rows change.  Entries of start / dom_pairs are not checked
  * on the host; out-of-range values give undefined cache contents, never a
  * write outside the cache.
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE (B, Hkv, S, Lmax < 1 or d not 64/128),
- *         SA_ERR_RANGE (theta <= 1, n_dom outside [1, d/2]), SA_ERR_DTYPE.
+ *         SA_ERR_RANGE (theta <= 1, n_dom outside [1, d/2]), SA_ERR_DTYPE,
+ *         SA_ERR_ACCESS (k_rest or v_cache in pageable host memory).
  */
 sa_status sa_kv_cache_append(const void* k_new, const void* v_new, sa_dtype dtype, int B,
                              int Hkv, int S, int d, int Lmax, const int32_t* start, double theta,
@@ -205,7 +215,10 @@ sa_status sa_sparse_attn_prefill(const void* q_rope, const void* k_rope, const v
  * selected tokens, at their original positions (the cache holds rotated keys).
  *   q_rope [B, Hq, d]; slab == 0: k [B, Hkv, Lmax, d]; slab == 1: k = k_dom
  *   and k_rest as in sa_token_score (both read; the full key is their
- *   channel union).  v [B, Hkv, Lmax, d].
+ *   channel union).  v [B, Hkv, Lmax, d].  k_rest and v may be pinned host
+ *   memory (host placement, FASA-M: only the dominant slab stays in device
+ *   memory and the selected rows of the rest are read over the host link
+ *   when they are needed).
  *   tok_idx [B, Hq, max_k] int32 token positions (< cache_len[b]), tok_cnt
  *   [B, Hq] in [0, max_k].
  *   cache_len is accepted for symmetry with sa_token_score and may be NULL:
@@ -217,7 +230,7 @@ sa_status sa_sparse_attn_prefill(const void* q_rope, const void* k_rope, const v
  *   accumulators) live in ws and are merged by the log-sum-exp rule.
  *   ws_bytes >= sa_workspace_bytes(SA_OP_DECODE, 0, 0, B, Hq, max_k).
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_RANGE, SA_ERR_WORKSPACE,
- *         SA_ERR_DTYPE.
+ *         SA_ERR_DTYPE, SA_ERR_ACCESS (k_rest or v in pageable host memory).
  */
 sa_status sa_sparse_attn_decode(const void* q_rope, const void* k, const void* k_rest,
                                 const void* v, sa_dtype dtype, int B, int Hq, int Hkv, int Lmax,

@@ -1,9 +1,10 @@
 """Python binding of the MI355X sparse-attention library (libsa_mi355x.so).
 
 Argument marshalling only: every function below takes torch tensors that
-already live on the GPU, checks their dtype/shape/contiguity, and passes raw
-device pointers, sizes and the current HIP stream to the C entry point of the
-same name.  All computation happens in the HIP kernels.  If the shared
+already live on the GPU (or, where an entry point allows host placement, in
+pinned host memory), checks their dtype/shape/contiguity, and passes raw
+pointers, sizes and the current HIP stream to the C entry point of the same
+name.  All computation happens in the HIP kernels.  If the shared
 library has not been built, importing this package raises ImportError; there
 is no CPU fallback.
 
@@ -18,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsa_mi355x.so")
 
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_RANGE, SA_ERR_WORKSPACE, \
-    SA_ERR_UNSUPPORTED, SA_ERR_HIP = range(8)
+    SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_ACCESS = range(9)
 SA_F32, SA_BF16 = 0, 1
 SA_OP_BLOCK_SCORE, SA_OP_TOPK, SA_OP_DECODE = 1, 2, 3
 
@@ -98,11 +99,13 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _check(t, name, dtype=None, ndim=None):
+def _check(t, name, dtype=None, ndim=None, host_ok=False):
+    """host_ok: pinned host tensors are accepted too (host placement of the
+    non-dominant keys and the values, FASA-M)."""
     if t is None:
         return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_cuda and not (host_ok and t.is_pinned()):
+        raise ValueError(f"{name} must be a GPU tensor" + (" or pinned host tensor" if host_ok else ""))
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -145,8 +148,8 @@ def sa_kv_cache_append(k_new, v_new, start, k_cache, v_cache, *, theta: float, k
     _check(v_new, "v_new", k_new.dtype, 4)
     _check(start, "start", torch.int32, 1)
     _check(k_cache, "k_cache", k_new.dtype, 4)
-    _check(k_rest, "k_rest", k_new.dtype, 4)
-    _check(v_cache, "v_cache", k_new.dtype, 4)
+    _check(k_rest, "k_rest", k_new.dtype, 4, host_ok=True)
+    _check(v_cache, "v_cache", k_new.dtype, 4, host_ok=True)
     _check(dom_pairs, "dom_pairs", torch.int32, 2)
     B, Hkv, S, d = k_new.shape
     if tuple(v_new.shape) != (B, Hkv, S, d) or start.shape[0] != B:
@@ -257,8 +260,8 @@ def sa_sparse_attn_decode(q_rope, k, v, tok_idx, tok_cnt, out, ws, *, sm_scale: 
     torch = _torch()
     _check(q_rope, "q_rope", ndim=3)
     _check(k, "k", q_rope.dtype, 4)
-    _check(k_rest, "k_rest", q_rope.dtype, 4)
-    _check(v, "v", q_rope.dtype, 4)
+    _check(k_rest, "k_rest", q_rope.dtype, 4, host_ok=True)
+    _check(v, "v", q_rope.dtype, 4, host_ok=True)
     _check(out, "out", q_rope.dtype, 3)
     _check(tok_idx, "tok_idx", torch.int32, 3)
     _check(tok_cnt, "tok_cnt", torch.int32, 2)

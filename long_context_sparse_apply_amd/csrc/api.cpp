@@ -23,6 +23,27 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
 
+// Device address of a buffer that may be pinned host memory (host placement
+// of the non-dominant keys and the values, FASA sec. 2.C).  Device memory is
+// used as it is; pinned host memory is replaced by its device mapping; host
+// memory the device cannot reach (pageable, not registered with HIP) is
+// refused, so no kernel ever dereferences it.
+static bool device_view(const void* p, const void** out) {
+  *out = p;
+  if (!p) return true;
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (a.type == hipMemoryTypeHost) {
+    if (!a.devicePointer) return false;
+    *out = a.devicePointer;
+    return true;
+  }
+  return a.type != hipMemoryTypeUnregistered;
+}
+
 extern "C" {
 
 sa_status sa_rope_apply(const void* x, void* out, sa_dtype dtype, int B, int H, int S, int d,
@@ -48,10 +69,14 @@ sa_status sa_kv_cache_append(const void* k_new, const void* v_new, sa_dtype dtyp
     if (n_dom < 1 || 2 * n_dom > d) return SA_ERR_RANGE;
     if (2 * n_dom < d && !k_rest) return SA_ERR_NULL;
   }
+  const void* kr = nullptr;
+  const void* vc = nullptr;
+  if (!device_view(k_rest, &kr) || !device_view(v_cache, &vc)) return SA_ERR_ACCESS;
   const sa::RopeFreq fr = sa::make_rope_freq(d, theta);
   return launched(sa::launch_kv_append(k_new, v_new, dtype, B, Hkv, S, d, Lmax, start, fr,
-                                       slab ? 1 : 0, dom_pairs, slab ? n_dom : 0, k_cache, k_rest,
-                                       v_cache, as_stream(stream)));
+                                       slab ? 1 : 0, dom_pairs, slab ? n_dom : 0, k_cache,
+                                       const_cast<void*>(kr), const_cast<void*>(vc),
+                                       as_stream(stream)));
 }
 
 sa_status sa_block_score(const void* q, const void* k, sa_dtype dtype, int B, int Hq, int Hkv,
@@ -158,6 +183,7 @@ sa_status sa_sparse_attn_decode(const void* q_rope, const void* k, const void* k
   }
   const size_t need = sa::decode_ws_bytes(B, Hq, max_k);
   if (!ws || ws_bytes < need) return SA_ERR_WORKSPACE;
+  if (!device_view(k_rest, &k_rest) || !device_view(v, &v)) return SA_ERR_ACCESS;
   return launched(sa::launch_decode(q_rope, k, k_rest, v, dtype, B, Hq, Hkv, Lmax, d, cache_len,
                                     dom_pairs, n_dom, slab ? 1 : 0, tok_idx, tok_cnt, max_k,
                                     sm_scale, out, lse, ws, as_stream(stream)));
@@ -189,6 +215,7 @@ const char* sa_status_string(sa_status s) {
     case SA_ERR_WORKSPACE: return "workspace missing or too small";
     case SA_ERR_UNSUPPORTED: return "unsupported configuration";
     case SA_ERR_HIP: return "HIP launch or runtime error";
+    case SA_ERR_ACCESS: return "buffer not accessible from the device (pageable host memory)";
   }
   return "unknown status";
 }

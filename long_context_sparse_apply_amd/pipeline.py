@@ -90,17 +90,26 @@ class DecodeCache:
     dominant slab ``k [B, Hkv, Lmax, 2*n_dom]`` plus ``k_rest [B, Hkv, Lmax,
     d - 2*n_dom]``.  ``lens`` (int32 [B], on the device) counts the rows
     written so far; appends go to row ``lens[b]`` onward.
+
+    ``host_rest`` (slab layout only): FASA's memory-optimised variant
+    (FASA-M, sec. 2.C).  Only the dominant slab stays in device memory;
+    ``k_rest`` and ``v`` live in pinned host memory, and the decode step
+    reads the selected rows of them over the host link when it attends.
     """
 
-    def __init__(self, B, Hkv, Lmax, d, *, dtype, device, theta, dom_pairs, slab=False):
+    def __init__(self, B, Hkv, Lmax, d, *, dtype, device, theta, dom_pairs, slab=False,
+                 host_rest=False):
+        if host_rest and not slab:
+            raise ValueError("host placement keeps the dominant slab on the device: needs slab")
         self.B, self.Hkv, self.Lmax, self.d = B, Hkv, Lmax, d
         self.theta, self.slab, self.dom = theta, slab, dom_pairs
         n_dom = dom_pairs.shape[1]
         kd = 2 * n_dom if slab else d
+        rest_kw = dict(device="cpu", pin_memory=True) if host_rest else dict(device=device)
         self.k = torch.zeros((B, Hkv, Lmax, kd), dtype=dtype, device=device)
-        self.k_rest = (torch.zeros((B, Hkv, Lmax, d - kd), dtype=dtype, device=device)
+        self.k_rest = (torch.zeros((B, Hkv, Lmax, d - kd), dtype=dtype, **rest_kw)
                        if slab and kd < d else None)
-        self.v = torch.zeros((B, Hkv, Lmax, d), dtype=dtype, device=device)
+        self.v = torch.zeros((B, Hkv, Lmax, d), dtype=dtype, **rest_kw)
         self.lens = torch.zeros(B, dtype=torch.int32, device=device)
 
     def append(self, k_new, v_new, batch=None):

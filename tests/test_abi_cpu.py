@@ -102,6 +102,15 @@ def test_validation_errors_before_launch():
                                    P(), P(), 512, 0.1, P(), None, P(), need, None) == sa.SA_ERR_UNSUPPORTED
     assert L.sa_sparse_attn_decode(P(), P(), None, P(), 1, 2, 8, 2, 1024, 128, P(), P(), 16, 1,
                                    P(), P(), 512, 0.1, P(), None, P(), need, None) == sa.SA_ERR_NULL
+    # host placement: k_rest / v may be pinned host memory, never pageable memory (refused
+    # before any launch; without a GPU no host memory is reachable either)
+    pageable = ctypes.create_string_buffer(1 << 16)
+    hp = ctypes.cast(pageable, ctypes.c_void_p)
+    assert L.sa_sparse_attn_decode(P(), P(), None, hp, 1, 2, 8, 2, 1024, 128, P(), None, 0, 0,
+                                   P(), P(), 512, 0.1, P(), None, P(), need, None) == sa.SA_ERR_ACCESS
+    assert L.sa_kv_cache_append(P(), P(), 1, 2, 2, 4, 128, 64, P(), 1e4, 0, None, 0, P(), None,
+                                hp, None) == sa.SA_ERR_ACCESS
+    assert "accessible" in sa.status_string(sa.SA_ERR_ACCESS)
 
 
 def test_workspace_sizes():

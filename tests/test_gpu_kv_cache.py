@@ -181,12 +181,15 @@ def test_kv_cache_append_standard_matches_rope_apply(sa):
         assert np.all((g >= lo) & (g <= hi))
 
 
-@pytest.mark.parametrize("slab", [False, True], ids=["std", "slab"])
-def test_prefill_decode_handoff(sa, slab):
+@pytest.mark.parametrize("slab,host_rest", [(False, False), (True, False), (True, True)],
+                         ids=["std", "slab", "slab-host-rest"])
+def test_prefill_decode_handoff(sa, slab, host_rest):
     """Two prompts (2048 and 1536 tokens) through the prefill layer into one
-    cache, then 3 decode steps with per-row positions, each against the oracle."""
+    cache, then 3 decode steps with per-row positions, each against the oracle.
+    With host_rest the non-dominant keys and the values live in pinned host
+    memory (FASA-M) and are written and read over the host link."""
     from long_context_sparse_apply_amd.pipeline import DecodeCache
-    say(f"case: prefill -> decode handoff slab={slab}")
+    say(f"case: prefill -> decode handoff slab={slab} host_rest={host_rest}")
     lens0 = [2048, 1536]
     T, top_k, n_dom = 3, 256, 16
     base = W.C2.with_(Hq=8, Hkv=2, needle_pairs=4)
@@ -194,7 +197,9 @@ def test_prefill_decode_handoff(sa, slab):
     Lmax = max(lens0) + T
     dom = _dom(Hkv, d, n_dom, 32)
     cache = DecodeCache(B, Hkv, Lmax, d, dtype=torch.bfloat16, device=DEV, theta=theta,
-                        dom_pairs=torch.from_numpy(dom).to(DEV), slab=slab)
+                        dom_pairs=torch.from_numpy(dom).to(DEV), slab=slab, host_rest=host_rest)
+    if host_rest:
+        assert not cache.v.is_cuda and cache.v.is_pinned() and cache.k_rest.is_pinned()
     cache.k.fill_(SENTINEL)
     cache.v.fill_(SENTINEL)
     if cache.k_rest is not None:
@@ -235,3 +240,32 @@ def test_prefill_decode_handoff(sa, slab):
         say(f"  step {t}: lens {lens.tolist()}")
         _compare_decode(dcfg, step, x, list(range(B)), list(range(Hkv)), k_amb=hi - lo)
     _check_cache(cache.k, cache.k_rest, cache.v, hc, "bf16", dom, slab)
+
+
+def test_decode_host_placement(sa):
+    """FASA-M placement on the decode step: the dominant slab in device memory,
+    the rest of each key and the values in pinned host memory.  The step must
+    equal the all-device step bit for bit (same kernels, same data) and match
+    the oracle."""
+    import synth.device as SD
+    from long_context_sparse_apply_amd.pipeline import DecodeStep
+    from tests.test_gpu_end_to_end import _decode_step
+    cfg = W.C5.with_(B=2, L=8192, k=256, ragged=1000)
+    say("case: decode with host-placed k_rest / v (slab-8k)")
+    x = W.decode_inputs_host(cfg)
+    dt = SD.decode_tensors(cfg)
+    dev_step = _decode_step(sa, cfg, x, dt)
+    dev_step.run()
+    k_rest_h = torch.empty(dt["k_rest"].shape, dtype=dt["k_rest"].dtype, pin_memory=True)
+    v_h = torch.empty(dt["v"].shape, dtype=dt["v"].dtype, pin_memory=True)
+    k_rest_h.copy_(dt["k_rest"])
+    v_h.copy_(dt["v"])
+    torch.cuda.synchronize()
+    host_step = DecodeStep(dt["q_raw"], dt["k"], v_h, dt["lens"], dt["dom"], theta=cfg.theta,
+                           top_k=cfg.k, slab=True, k_rest=k_rest_h)
+    host_step.run()
+    torch.cuda.synchronize()
+    assert torch.equal(host_step.tok_idx, dev_step.tok_idx)
+    assert torch.equal(host_step.out, dev_step.out)
+    assert torch.equal(host_step.lse, dev_step.lse)
+    _compare_decode(cfg, host_step, x, list(range(cfg.B)), list(range(cfg.Hkv)))
