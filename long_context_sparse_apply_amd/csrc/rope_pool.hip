@@ -113,27 +113,61 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(
   __shared__ float s_band[2][2];  // [band][0: energy sum, 1: pooled sq sum]
   __shared__ float s_fac[2];
 
-  // cos / sin of this thread's (row, pair) grid
+  // cos / sin of this thread's (row, pair) grid (rows past the block are
+  // computed too and never used); the 8 frequencies are read once, together
+  double fj[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) fj[j] = fr.f[8 * c + j];
   float cs[MAXR][8], sn[MAXR][8];
 #pragma unroll
   for (int ri = 0; ri < MAXR; ++ri) {
-    const int r = r0 + ri * RP;
-    const int64_t p = static_cast<int64_t>(I) * block + r;
+    const int64_t p = static_cast<int64_t>(I) * block + r0 + ri * RP;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (r < block) rot_cos_sin(p, fr.f[8 * c + j], cs[ri][j], sn[ri][j]);
-      else { cs[ri][j] = 1.f; sn[ri][j] = 0.f; }
-    }
+    for (int j = 0; j < 8; ++j) rot_cos_sin(p, fj[j], cs[ri][j], sn[ri][j]);
   }
+
+  // the block's rows of head row hr (KV head first, then the group's query heads)
+  auto head_src = [&](int hr) {
+    const bool is_k = (hr == 0);
+    const int h = is_k ? g : g * grp + (hr - 1);
+    const int H = is_k ? Hkv : Hq;
+    return (is_k ? k : q) + ((static_cast<int64_t>(b) * H + h) * S + static_cast<int64_t>(I) * block) * D;
+  };
+  // this thread's raw elements of one head row; the next head's are loaded
+  // before the current head's reductions, so its loads are in flight while
+  // the work-group reduces
+  using Raw = typename Elem<T>::Raw;
+  Raw nxt_a[MAXR], nxt_b[MAXR];
+  auto load_head = [&](int hr) {
+    const T* src = head_src(hr);
+#pragma unroll
+    for (int ri = 0; ri < MAXR; ++ri) {
+      const int r = r0 + ri * RP;
+      if (r < block) {
+        nxt_a[ri] = Elem<T>::load_raw8(src + static_cast<int64_t>(r) * D + 8 * c);
+        nxt_b[ri] = Elem<T>::load_raw8(src + static_cast<int64_t>(r) * D + P + 8 * c);
+      } else {
+        nxt_a[ri] = Elem<T>::zero_raw8();
+        nxt_b[ri] = Elem<T>::zero_raw8();
+      }
+    }
+  };
+  // barrier for the LDS reductions only: waits for this wave's LDS accesses,
+  // not for its global loads (the next head's rows stay in flight)
+  auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  load_head(0);
 
   for (int hr = 0; hr <= grp; ++hr) {
     const bool is_k = (hr == 0);
     const int h = is_k ? g : g * grp + (hr - 1);
     const int H = is_k ? Hkv : Hq;
-    const T* src = (is_k ? k : q) + ((static_cast<int64_t>(b) * H + h) * S + static_cast<int64_t>(I) * block) * D;
     T* dst = is_k ? k_rope : q_rope;
     if (dst) dst += ((static_cast<int64_t>(b) * H + h) * S + static_cast<int64_t>(I) * block) * D;
     float* pool_out = (is_k ? pk : pq) + ((static_cast<int64_t>(b) * H + h) * N + I) * D;
+    Raw cur_a[MAXR], cur_b[MAXR];
+#pragma unroll
+    for (int ri = 0; ri < MAXR; ++ri) { cur_a[ri] = nxt_a[ri]; cur_b[ri] = nxt_b[ri]; }
+    if (hr < grp) load_head(hr + 1);
 
     float col[16];
 #pragma unroll
@@ -144,8 +178,8 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(
       const int r = r0 + ri * RP;
       if (r < block) {
         float a[8], bb[8], ra[8], rb[8];
-        Elem<T>::load8(src + static_cast<int64_t>(r) * D + 8 * c, a);
-        Elem<T>::load8(src + static_cast<int64_t>(r) * D + P + 8 * c, bb);
+        Elem<T>::unpack8(cur_a[ri], a);
+        Elem<T>::unpack8(cur_b[ri], bb);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           ra[j] = a[j] * cs[ri][j] - bb[j] * sn[ri][j];
@@ -173,7 +207,7 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(
       s_red[0][tid / kWave] = e_hi;
       s_red[1][tid / kWave] = e_lo;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < D) {
       float sum = 0.f;
       for (int r = 0; r < RP; ++r) sum += s_col[r][tid];
@@ -184,7 +218,7 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(
       for (int w = 0; w < 256 / kWave; ++w) e += s_red[tid][w];
       s_band[tid][0] = e;
     }
-    __syncthreads();
+    lds_barrier();
     // pooled squared norms per band
     {
       float v = 0.f;
@@ -203,7 +237,7 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(
         s_red[1][tid / kWave] = lo;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < 2) {
       float m2 = 0.f;
       for (int w = 0; w < 256 / kWave; ++w) m2 += s_red[tid][w];
@@ -220,12 +254,12 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(
       }
       s_fac[tid] = fac;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < D) {
       const int pair = tid % P;
       pool_out[tid] = s_m[tid] * s_fac[pair < split ? 0 : 1];
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
