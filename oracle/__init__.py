@@ -13,7 +13,9 @@ Sources (web summaries of two papers):
 * "FASA: Frequency-aware Sparse Attention" -- frequency chunks (sec. 2.A),
   the Token Importance Predictor and Focused Attention Computation
   (sec. 2.B), the computation-optimised variant that keeps only a sparse
-  subset of key states on the read path (sec. 2.C).
+  subset of key states on the read path (sec. 2.C), and the one-time offline
+  calibration of the dominant chunks (sec. 2.B item 1; criterion read here,
+  see ``oracle/calibration.py``).
 
 Neither page prints a formula for these steps; the readings taken here are
 listed at each function.  Parity of the calibration formula and of the band
@@ -24,4 +26,7 @@ from .sparse_attention import (  # noqa: F401
     rope_frequencies, rope, band_channels, pool_blocks, block_scores, select_row, select_rows,
     prefill_attention, decode_query, token_scores, decode_attention, slab_to_standard,
     standard_to_slab, prefill_pipeline, decode_pipeline, keep_budget,
+)
+from .calibration import (  # noqa: F401
+    calibration_scores, topk_set, overlap_counts, calibrate_dominant,
 )

@@ -352,3 +352,74 @@ def decode_patches(cfg: DecodeConfig, lens: np.ndarray):
         for p in ps:
             out.append((b, h, p, stored))
     return out
+
+
+# ---------------------------------------------------------------- calibration
+@dataclass(frozen=True)
+class CalibConfig:
+    """Offline calibration of the dominant rotary pairs (FASA sec. 2.B item 1:
+    a one-time calibration identifies the dominant frequency chunks).
+
+    Inputs are rotated calibration queries q [Hq, M, d] and keys k [Hkv, L, d]
+    (stored bf16).  Each KV head gets a planted dominant set of n_dom pairs:
+    for every calibration query, k_cal / 2 keys of the window (disjoint
+    between the group's queries) receive amp times the unit direction of that
+    query's components on the planted pairs, on those pairs only.  The rest
+    is Irwin-Hall(12) noise.
+    """
+    name: str
+    Hq: int
+    Hkv: int
+    M: int
+    L: int
+    d: int
+    n_dom: int
+    k_cal: int
+    amp: float = 12.0
+    seed: int = 9
+    dtype: str = "bf16"
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    def with_(self, **kw) -> "CalibConfig":
+        return dataclasses.replace(self, **kw)
+
+
+CAL_SMALL = CalibConfig("calibration, 8 query / 2 KV heads, 8 queries, window 2048, d=128", 8, 2,
+                        8, 2048, 128, n_dom=16, k_cal=64)
+CAL_LLAMA = CalibConfig("calibration, Llama-3.1-8B-shaped heads, 16 queries, window 4096, d=128",
+                        32, 8, 16, 4096, 128, n_dom=16, k_cal=256)
+
+
+def planted_pairs(cfg: CalibConfig) -> np.ndarray:
+    """[Hkv, n_dom] ascending distinct rotary pairs planted as dominant."""
+    P = cfg.d // 2
+    out = np.empty((cfg.Hkv, cfg.n_dom), np.int32)
+    for g in range(cfg.Hkv):
+        u = uniform01(cfg.seed, TID_DOM, np.arange(g * P, (g + 1) * P, dtype=np.uint64))
+        out[g] = np.sort(np.argsort(u, kind="stable")[: cfg.n_dom])
+    return out
+
+
+def calibration_inputs_host(cfg: CalibConfig):
+    """(q [Hq, M, d], k [Hkv, L, d], planted [Hkv, n_dom]) as stored values."""
+    P = cfg.d // 2
+    r = cfg.k_cal // 2
+    if cfg.group * cfg.M * r > cfg.L:
+        raise ValueError("window too short for disjoint relevant key sets")
+    q = gaussian_tensor(cfg.seed, TID_Q, (cfg.Hq, cfg.M, cfg.d), cfg.dtype).astype(np.float64)
+    k = gaussian_tensor(cfg.seed, TID_K, (cfg.Hkv, cfg.L, cfg.d), cfg.dtype).astype(np.float64)
+    dom = planted_pairs(cfg)
+    for g in range(cfg.Hkv):
+        ch = np.concatenate([dom[g], dom[g] + P]).astype(np.int64)
+        u = uniform01(cfg.seed, TID_NEEDLE, (g << 24) + np.arange(cfg.L, dtype=np.uint64))
+        perm = np.argsort(u, kind="stable")
+        for hh in range(cfg.group):
+            h = g * cfg.group + hh
+            for m in range(cfg.M):
+                keys = perm[(hh * cfg.M + m) * r:(hh * cfg.M + m + 1) * r]
+                dirn = q[h, m, ch] / np.linalg.norm(q[h, m, ch])
+                k[g, keys[:, None], ch[None, :]] += cfg.amp * dirn[None, :]
+    return _store(q, cfg.dtype), _store(k, cfg.dtype), dom
