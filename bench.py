@@ -197,6 +197,33 @@ def run_decode_host_rest(cfg, steps, warmup, torch, flush):
     return t
 
 
+def run_calibration(cfg, steps, warmup, torch, flush):
+    """The one-time calibration of the dominant pairs (FASA sec. 2.B item 1)
+    on a Llama-shaped window.  Algorithmic bytes: the keys and queries read
+    once, the full and pair scores written once and read once by the top-k,
+    their selections written once and read once by the overlap count."""
+    from long_context_sparse_apply_amd import calibrate_workspace_bytes, sa_calibrate_dominant
+    from synth import workloads as W
+    q, k, planted = W.calibration_inputs_host(cfg)
+    qt = torch.from_numpy(q).to("cuda").to(torch.bfloat16)
+    kt = torch.from_numpy(k).to("cuda").to(torch.bfloat16)
+    ws = torch.empty(calibrate_workspace_bytes(cfg.Hq, cfg.Hkv, cfg.M, cfg.L, cfg.d, cfg.k_cal),
+                     dtype=torch.uint8, device="cuda")
+    dom = torch.empty((cfg.Hkv, cfg.n_dom), dtype=torch.int32, device="cuda")
+    counts = torch.empty((cfg.Hkv, cfg.d // 2), dtype=torch.int32, device="cuda")
+
+    def fn():
+        sa_calibrate_dominant(qt, kt, dom, counts, ws, k_cal=cfg.k_cal)
+    med, p10, p90 = time_call(fn, steps, warmup, torch, flush)
+    rows = cfg.Hq * cfg.M * (cfg.d // 2 + 1)
+    nbytes = (qt.numel() + kt.numel()) * 2 + 2.0 * rows * cfg.L * 4 + 2.0 * rows * cfg.k_cal * 4
+    recovered = bool((dom.cpu().numpy() == planted).all())
+    del qt, kt, ws
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "us": med, "us_p10_p90": [p10, p90], "bytes": nbytes,
+            "hbm_frac": nbytes / (med * 1e-6) / PEAK_HBM_BPS, "planted_set_recovered": recovered}
+
+
 def run_cache_append(cfg_p, cfg_d, steps, warmup, torch, flush):
     """sa_kv_cache_append at its two uses: the prefill -> decode handoff (the
     whole prompt's keys rotated and values copied into a decode cache) and one
@@ -430,6 +457,10 @@ def main():
             "host_link_bytes": rm["host_link_bytes"], "host_link_GBps": rm["host_link_GBps"],
             "device_resident_bytes": rm["device_resident_bytes"],
             "host_resident_bytes": rm["host_resident_bytes"]}
+        log("calibration of the dominant pairs")
+        rc = run_calibration(W.CAL_LLAMA, max(3, args.steps // 4), 1, torch, flush)
+        log(json.dumps(rc))
+        secondary["calibration"] = rc
         log("cache append (prefill -> decode handoff, decode token)")
         ra = run_cache_append(cfg, W.C5, args.steps, args.warmup, torch, flush)
         log(json.dumps(ra))

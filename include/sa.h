@@ -240,6 +240,44 @@ sa_status sa_sparse_attn_decode(const void* q_rope, const void* k, const void* k
                                 float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sa_calibrate_dominant -- one-time offline calibration of the dominant
+ * rotary pairs of every KV head.  FASA sec. 2.A (a small fixed set of
+ * dominant frequency chunks reproduces a head's context selection) and sec.
+ * 2.B item 1 (the set comes from a one-time offline calibration).  The pages
+ * give no criterion; the one computed here:
+ *   for each query head h and calibration query m, the full score of key t
+ *   is sum_c q_c k_{t,c} and pair i's partial score is
+ *   q_i k_{t,i} + q_{i+P} k_{t,i+P} (P = d/2); pair i's overlap is the number
+ *   of keys its partial-score top-k_cal shares with the full-score
+ *   top-k_cal (top-k by score descending, then key ascending);
+ *   counts_out[g][i] = sum of the overlaps of pair i over the query heads of
+ *   KV head g and all calibration queries;
+ *   dom_out[g] = the n_dom pairs with the largest counts (ties to the lower
+ *   pair), ascending -- the dom_pairs argument of sa_token_score.
+ * Scores are decided in fp32: the full score adds the channel products in
+ * ascending channel order, a pair score is one rounding of its two products
+ * (with bf16 inputs every product is exact, so the result does not depend
+ * on the launch).
+ *   q_rope : [Hq, M, d] bf16, M rotated calibration queries per query head.
+ *   k_rope : [Hkv, L, d] bf16, the rotated keys of the calibration window
+ *            (every key is visible to every calibration query).
+ *   dom_out [Hkv, n_dom] int32, counts_out [Hkv, d/2] int32 (device).
+ *   ws_bytes >= sa_calibrate_workspace_bytes(Hq, Hkv, M, L, d, k_cal): the
+ *   full and pair scores, their selections and the counts.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE (sizes < 1, Hq % Hkv, d not 64/128,
+ *         L > 262144), SA_ERR_RANGE (k_cal outside [1, L], n_dom outside
+ *         [1, d/2]), SA_ERR_UNSUPPORTED (dtype other than SA_BF16),
+ *         SA_ERR_WORKSPACE, SA_ERR_DTYPE.
+ */
+sa_status sa_calibrate_dominant(const void* q_rope, const void* k_rope, sa_dtype dtype, int Hq,
+                                int Hkv, int M, int L, int d, int k_cal, int n_dom,
+                                int32_t* dom_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* Workspace bytes of sa_calibrate_dominant (0 for sizes it rejects). */
+size_t sa_calibrate_workspace_bytes(int Hq, int Hkv, int M, int L, int d, int k_cal);
+
+/*
  * sa_workspace_bytes -- bytes of workspace an operation needs.
  *   SA_OP_BLOCK_SCORE: rows = number of pooled vectors B*(Hq+Hkv)*N,
  *       cols = d -> scratch for the pooled Q and K vectors.

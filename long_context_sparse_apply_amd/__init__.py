@@ -25,7 +25,8 @@ SA_OP_BLOCK_SCORE, SA_OP_TOPK, SA_OP_DECODE = 1, 2, 3
 
 EXPORTED = ("sa_rope_apply", "sa_kv_cache_append", "sa_block_score", "sa_token_score",
             "sa_topk_select", "sa_sparse_attn_prefill", "sa_sparse_attn_decode",
-            "sa_workspace_bytes", "sa_status_string", "sa_version")
+            "sa_calibrate_dominant", "sa_calibrate_workspace_bytes", "sa_workspace_bytes",
+            "sa_status_string", "sa_version")
 
 
 class SAError(RuntimeError):
@@ -49,6 +50,8 @@ def _load() -> ctypes.CDLL:
         "sa_sparse_attn_prefill": [P, P, P, I, I, I, I, I, I, I, P, P, I, I, F, P, P, P],
         "sa_sparse_attn_decode": [P, P, P, P, I, I, I, I, I, I, P, P, I, I, P, P, I, F, P, P, P,
                                   SZ, P],
+        "sa_calibrate_dominant": [P, P, I, I, I, I, I, I, I, I, P, P, P, SZ, P],
+        "sa_calibrate_workspace_bytes": [I, I, I, I, I, I],
         "sa_workspace_bytes": [I, I64, I, I, I, I],
         "sa_status_string": [I],
         "sa_version": [],
@@ -58,6 +61,7 @@ def _load() -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = I
     lib.sa_workspace_bytes.restype = SZ
+    lib.sa_calibrate_workspace_bytes.restype = SZ
     lib.sa_status_string.restype = ctypes.c_char_p
     return lib
 
@@ -276,6 +280,29 @@ def sa_sparse_attn_decode(q_rope, k, v, tok_idx, tok_cnt, out, ws, *, sm_scale: 
           int(bool(slab)), _ptr(tok_idx), _ptr(tok_cnt), tok_idx.shape[-1], float(sm_scale),
           _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
     return out
+
+
+def calibrate_workspace_bytes(Hq: int, Hkv: int, M: int, L: int, d: int, k_cal: int) -> int:
+    return int(lib.sa_calibrate_workspace_bytes(Hq, Hkv, M, L, d, k_cal))
+
+
+def sa_calibrate_dominant(q_rope, k_rope, dom_out, counts_out, ws, *, k_cal: int, stream=None):
+    """q_rope [Hq, M, d], k_rope [Hkv, L, d] (bf16, rotated) -> dom_out [Hkv, n_dom],
+    counts_out [Hkv, d/2] (int32): the offline calibration of the dominant pairs."""
+    torch = _torch()
+    _check(q_rope, "q_rope", ndim=3)
+    _check(k_rope, "k_rope", q_rope.dtype, 3)
+    _check(dom_out, "dom_out", torch.int32, 2)
+    _check(counts_out, "counts_out", torch.int32, 2)
+    _check(ws, "ws")
+    Hq, M, d = q_rope.shape
+    Hkv, L = k_rope.shape[0], k_rope.shape[1]
+    if k_rope.shape[2] != d or dom_out.shape[0] != Hkv or tuple(counts_out.shape) != (Hkv, d // 2):
+        raise ValueError("q_rope / k_rope / dom_out / counts_out shapes disagree")
+    _call("sa_calibrate_dominant", _ptr(q_rope), _ptr(k_rope), _dtype_code(q_rope), Hq, Hkv, M, L,
+          d, int(k_cal), dom_out.shape[1], _ptr(dom_out), _ptr(counts_out), _ptr(ws),
+          ws.numel() * ws.element_size(), _stream(stream))
+    return dom_out, counts_out
 
 
 # ----------------------------------------------------------------------------- setup helpers

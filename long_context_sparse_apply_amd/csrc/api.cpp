@@ -189,6 +189,30 @@ sa_status sa_sparse_attn_decode(const void* q_rope, const void* k, const void* k
                                     sm_scale, out, lse, ws, as_stream(stream)));
 }
 
+static bool calib_sizes_ok(int Hq, int Hkv, int M, int L, int d) {
+  return Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && M >= 1 && L >= 1 && L <= 262144 &&
+         head_dim_ok(d);
+}
+
+sa_status sa_calibrate_dominant(const void* q_rope, const void* k_rope, sa_dtype dtype, int Hq,
+                                int Hkv, int M, int L, int d, int k_cal, int n_dom,
+                                int32_t* dom_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!dtype_ok(dtype)) return SA_ERR_DTYPE;
+  if (!q_rope || !k_rope || !dom_out || !counts_out) return SA_ERR_NULL;
+  if (!calib_sizes_ok(Hq, Hkv, M, L, d)) return SA_ERR_SHAPE;
+  if (k_cal < 1 || k_cal > L || n_dom < 1 || n_dom > d / 2) return SA_ERR_RANGE;
+  if (dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < sa::calib_ws_bytes(Hq, M, L, d, Hkv, k_cal)) return SA_ERR_WORKSPACE;
+  return launched(sa::launch_calibrate(q_rope, k_rope, Hq, Hkv, M, L, d, k_cal, n_dom, dom_out,
+                                       counts_out, ws, as_stream(stream)));
+}
+
+size_t sa_calibrate_workspace_bytes(int Hq, int Hkv, int M, int L, int d, int k_cal) {
+  if (!calib_sizes_ok(Hq, Hkv, M, L, d) || k_cal < 1 || k_cal > L) return 0;
+  return sa::calib_ws_bytes(Hq, M, L, d, Hkv, k_cal);
+}
+
 size_t sa_workspace_bytes(int op, int64_t rows, int cols, int B, int Hq, int max_k) {
   switch (op) {
     case SA_OP_BLOCK_SCORE:

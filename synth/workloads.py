@@ -389,8 +389,8 @@ class CalibConfig:
 
 CAL_SMALL = CalibConfig("calibration, 8 query / 2 KV heads, 8 queries, window 2048, d=128", 8, 2,
                         8, 2048, 128, n_dom=16, k_cal=64)
-CAL_LLAMA = CalibConfig("calibration, Llama-3.1-8B-shaped heads, 16 queries, window 4096, d=128",
-                        32, 8, 16, 4096, 128, n_dom=16, k_cal=256)
+CAL_LLAMA = CalibConfig("calibration, Llama-3.1-8B-shaped heads, 16 queries, window 8192, d=128",
+                        32, 8, 16, 8192, 128, n_dom=16, k_cal=256)
 
 
 def planted_pairs(cfg: CalibConfig) -> np.ndarray:

@@ -111,6 +111,27 @@ def test_validation_errors_before_launch():
     assert L.sa_kv_cache_append(P(), P(), 1, 2, 2, 4, 128, 64, P(), 1e4, 0, None, 0, P(), None,
                                 hp, None) == sa.SA_ERR_ACCESS
     assert "accessible" in sa.status_string(sa.SA_ERR_ACCESS)
+    # calibration of the dominant pairs: sizes, ranges, bf16 only, workspace
+    need = sa.calibrate_workspace_bytes(8, 2, 4, 2048, 128, 64)
+    assert need > 8 * 4 * 64 * 2048 * 4
+    assert sa.calibrate_workspace_bytes(8, 3, 4, 2048, 128, 64) == 0
+    assert sa.calibrate_workspace_bytes(8, 2, 4, 2048, 128, 4096) == 0
+    def cal(q=True, Hq=8, Hkv=2, M=4, L=2048, d=128, kc=64, nd=16, dtype=1, ws=True, wsb=None):
+        return L_.sa_calibrate_dominant(P() if q else None, P(), dtype, Hq, Hkv, M, L, d, kc, nd,
+                                        P(), P(), P() if ws else None,
+                                        need if wsb is None else wsb, None)
+    L_ = L
+    assert cal(q=False) == sa.SA_ERR_NULL
+    assert cal(Hkv=3) == sa.SA_ERR_SHAPE
+    assert cal(d=96) == sa.SA_ERR_SHAPE
+    assert cal(L=300000) == sa.SA_ERR_SHAPE
+    assert cal(kc=0) == sa.SA_ERR_RANGE
+    assert cal(kc=2049) == sa.SA_ERR_RANGE
+    assert cal(nd=65) == sa.SA_ERR_RANGE
+    assert cal(dtype=0) == sa.SA_ERR_UNSUPPORTED
+    assert cal(dtype=9) == sa.SA_ERR_DTYPE
+    assert cal(ws=False) == sa.SA_ERR_WORKSPACE
+    assert cal(wsb=need - 1) == sa.SA_ERR_WORKSPACE
 
 
 def test_workspace_sizes():
