@@ -224,6 +224,35 @@ def run_calibration(cfg, steps, warmup, torch, flush):
             "hbm_frac": nbytes / (med * 1e-6) / PEAK_HBM_BPS, "planted_set_recovered": recovered}
 
 
+def run_sfa(steps, warmup, torch, flush, S=8192, Hq=32, Hkv=8, d=128, kf=16):
+    """Sparse Feature Attention over one causal prefill layer: k-sparse codes
+    of Q and K, then exact attention over every causal block of the codes on
+    the matrix unit.  FLOPs counted as the kernel performs them: 4 d per
+    visible (query, key) pair."""
+    import synth
+    import synth.device as SD
+    from long_context_sparse_apply_amd.pipeline import SFALayer
+    q = torch.empty((1, Hq, S, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((1, Hkv, S, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    SD.fill(q, 23, synth.TID_Q)
+    SD.fill(k, 23, synth.TID_K)
+    SD.fill(v, 23, synth.TID_V)
+    layer = SFALayer(q, k, v, k_feat=kf)
+    codes = time_call(layer.codes, steps, warmup, torch, flush)
+    attend = time_call(layer.attend, steps, warmup, torch, flush)
+    flops = 4.0 * d * Hq * S * (S + 1) / 2
+    res = {"workload": f"SFA causal prefill, {Hq} query / {Hkv} KV heads, {S} tokens, d={d}, "
+                       f"k={kf} active channels per token, bf16",
+           "codes_us": codes[0], "attend_ms": attend[0] / 1e3,
+           "tok_per_s": S / ((codes[0] + attend[0]) * 1e-6),
+           "attend_tflops": flops / (attend[0] * 1e-6) / 1e12,
+           "attend_mfma_frac": flops / (attend[0] * 1e-6) / PEAK_BF16_FLOPS}
+    del layer, q, k, v
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_cache_append(cfg_p, cfg_d, steps, warmup, torch, flush):
     """sa_kv_cache_append at its two uses: the prefill -> decode handoff (the
     whole prompt's keys rotated and values copied into a decode cache) and one
@@ -457,6 +486,10 @@ def main():
             "host_link_bytes": rm["host_link_bytes"], "host_link_GBps": rm["host_link_GBps"],
             "device_resident_bytes": rm["device_resident_bytes"],
             "host_resident_bytes": rm["host_resident_bytes"]}
+        log("sfa_prefill_8k (Sparse Feature Attention)")
+        rs = run_sfa(max(3, args.steps // 4), 1, torch, flush)
+        log(json.dumps(rs))
+        secondary["sfa_prefill_8k"] = rs
         log("calibration of the dominant pairs")
         rc = run_calibration(W.CAL_LLAMA, max(3, args.steps // 4), 1, torch, flush)
         log(json.dumps(rc))

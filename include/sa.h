@@ -274,6 +274,21 @@ sa_status sa_calibrate_dominant(const void* q_rope, const void* k_rope, sa_dtype
                                 int32_t* dom_out, int32_t* counts_out, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/*
+ * sa_sfa_sparsify -- k-sparse feature codes for Sparse Feature Attention
+ * ("Scaling Attention via Feature Sparsity", sec. 2): every row of x keeps
+ * its k_feat channels of largest magnitude (ties to the lower channel, NaN
+ * below every number) and zeroes the others.  Attention over the codes is
+ * sa_sparse_attn_prefill with every causal block listed: the dot product of
+ * two zero-filled codes is the sum over the channels active in both.
+ *   x, out : [rows, d] dtype (out may equal x); values are copied bit for bit.
+ *   k_feat >= d keeps every channel; k_feat == 0 zeroes the row.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE (rows < 0, d not 64/128),
+ *         SA_ERR_RANGE (k_feat < 0), SA_ERR_DTYPE.
+ */
+sa_status sa_sfa_sparsify(const void* x, void* out, sa_dtype dtype, int64_t rows, int d,
+                          int k_feat, void* stream);
+
 /* Workspace bytes of sa_calibrate_dominant (0 for sizes it rejects). */
 size_t sa_calibrate_workspace_bytes(int Hq, int Hkv, int M, int L, int d, int k_cal);
 

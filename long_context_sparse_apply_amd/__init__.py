@@ -25,7 +25,8 @@ SA_OP_BLOCK_SCORE, SA_OP_TOPK, SA_OP_DECODE = 1, 2, 3
 
 EXPORTED = ("sa_rope_apply", "sa_kv_cache_append", "sa_block_score", "sa_token_score",
             "sa_topk_select", "sa_sparse_attn_prefill", "sa_sparse_attn_decode",
-            "sa_calibrate_dominant", "sa_calibrate_workspace_bytes", "sa_workspace_bytes",
+            "sa_calibrate_dominant", "sa_calibrate_workspace_bytes", "sa_sfa_sparsify",
+            "sa_workspace_bytes",
             "sa_status_string", "sa_version")
 
 
@@ -52,6 +53,7 @@ def _load() -> ctypes.CDLL:
                                   SZ, P],
         "sa_calibrate_dominant": [P, P, I, I, I, I, I, I, I, I, P, P, P, SZ, P],
         "sa_calibrate_workspace_bytes": [I, I, I, I, I, I],
+        "sa_sfa_sparsify": [P, P, I, I64, I, I, P],
         "sa_workspace_bytes": [I, I64, I, I, I, I],
         "sa_status_string": [I],
         "sa_version": [],
@@ -303,6 +305,18 @@ def sa_calibrate_dominant(q_rope, k_rope, dom_out, counts_out, ws, *, k_cal: int
           d, int(k_cal), dom_out.shape[1], _ptr(dom_out), _ptr(counts_out), _ptr(ws),
           ws.numel() * ws.element_size(), _stream(stream))
     return dom_out, counts_out
+
+
+def sa_sfa_sparsify(x, out, *, k_feat: int, stream=None):
+    """x, out [..., d] (out may be x): k-sparse feature codes of every row."""
+    _check(x, "x")
+    _check(out, "out", x.dtype)
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    d = x.shape[-1]
+    _call("sa_sfa_sparsify", _ptr(x), _ptr(out), _dtype_code(x), x.numel() // d, d, int(k_feat),
+          _stream(stream))
+    return out
 
 
 # ----------------------------------------------------------------------------- setup helpers

@@ -208,6 +208,16 @@ sa_status sa_calibrate_dominant(const void* q_rope, const void* k_rope, sa_dtype
                                        counts_out, ws, as_stream(stream)));
 }
 
+sa_status sa_sfa_sparsify(const void* x, void* out, sa_dtype dtype, int64_t rows, int d,
+                          int k_feat, void* stream) {
+  if (!dtype_ok(dtype)) return SA_ERR_DTYPE;
+  if (rows < 0 || !head_dim_ok(d)) return SA_ERR_SHAPE;
+  if (k_feat < 0) return SA_ERR_RANGE;
+  if (rows == 0) return SA_OK;
+  if (!x || !out) return SA_ERR_NULL;
+  return launched(sa::launch_sfa_sparsify(x, out, dtype, rows, d, k_feat, as_stream(stream)));
+}
+
 size_t sa_calibrate_workspace_bytes(int Hq, int Hkv, int M, int L, int d, int k_cal) {
   if (!calib_sizes_ok(Hq, Hkv, M, L, d) || k_cal < 1 || k_cal > L) return 0;
   return sa::calib_ws_bytes(Hq, M, L, d, Hkv, k_cal);

@@ -61,6 +61,10 @@ hipError_t launch_decode(const void* q, const void* k, const void* k_rest, const
                          const int32_t* tok_idx, const int32_t* tok_cnt, int max_k, float scale,
                          void* out, float* lse, void* ws, hipStream_t st);
 
+// k-sparse feature codes (Sparse Feature Attention)
+hipError_t launch_sfa_sparsify(const void* x, void* out, int dtype, int64_t rows, int d, int kf,
+                               hipStream_t st);
+
 // offline calibration of the dominant pairs (scores, selections, overlaps)
 size_t calib_ws_bytes(int Hq, int M, int L, int d, int Hkv, int kcal);
 hipError_t launch_calibrate(const void* q, const void* k, int Hq, int Hkv, int M, int L, int d,

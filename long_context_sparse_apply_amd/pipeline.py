@@ -20,8 +20,8 @@ from __future__ import annotations
 import torch
 
 from . import (SA_OP_BLOCK_SCORE, SA_OP_DECODE, prefill_row_params, sa_block_score,
-               sa_kv_cache_append, sa_rope_apply, sa_sparse_attn_decode, sa_sparse_attn_prefill,
-               sa_token_score, sa_topk_select, workspace_bytes)
+               sa_kv_cache_append, sa_rope_apply, sa_sfa_sparsify, sa_sparse_attn_decode,
+               sa_sparse_attn_prefill, sa_token_score, sa_topk_select, workspace_bytes)
 
 
 class PrefillLayer:
@@ -78,6 +78,45 @@ class PrefillLayer:
     def run(self):
         self.score()
         self.select()
+        self.attend()
+        return self.out
+
+
+class SFALayer:
+    """Sparse Feature Attention ("Scaling Attention via Feature Sparsity",
+    sec. 2) over one causal prefill layer: k-sparse codes of Q and K
+    (sa_sfa_sparsify), then exact attention over every causal block of the
+    codes (sa_sparse_attn_prefill with the full causal block list, built once
+    per shape)."""
+
+    def __init__(self, q, k, v, *, k_feat, block=128, sm_scale=None):
+        self.q, self.k, self.v = q, k, v
+        B, Hq, S, d = q.shape
+        self.block, self.N, self.k_feat = block, S // block, k_feat
+        self.scale = sm_scale if sm_scale is not None else d ** -0.5
+        dev = q.device
+        N = self.N
+        self.q_code = torch.empty_like(q)
+        self.k_code = torch.empty_like(k)
+        # every block J <= I of query block I (the kernel skips J > I when causal)
+        self.blk_idx = torch.arange(N, dtype=torch.int32, device=dev).repeat(B * Hq * N).view(
+            B, Hq, N, N).contiguous()
+        self.blk_cnt = torch.arange(1, N + 1, dtype=torch.int32, device=dev).repeat(B * Hq).view(
+            B, Hq, N).contiguous()
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+
+    def codes(self):
+        sa_sfa_sparsify(self.q, self.q_code, k_feat=self.k_feat)
+        sa_sfa_sparsify(self.k, self.k_code, k_feat=self.k_feat)
+
+    def attend(self):
+        sa_sparse_attn_prefill(self.q_code, self.k_code, self.v, self.blk_idx, self.blk_cnt,
+                               self.out, block=self.block, sm_scale=self.scale, causal=True,
+                               lse=self.lse)
+
+    def run(self):
+        self.codes()
         self.attend()
         return self.out
 

@@ -132,6 +132,13 @@ def test_validation_errors_before_launch():
     assert cal(dtype=9) == sa.SA_ERR_DTYPE
     assert cal(ws=False) == sa.SA_ERR_WORKSPACE
     assert cal(wsb=need - 1) == sa.SA_ERR_WORKSPACE
+    # k-sparse feature codes
+    assert L.sa_sfa_sparsify(P(), P(), 1, -1, 128, 16, None) == sa.SA_ERR_SHAPE
+    assert L.sa_sfa_sparsify(P(), P(), 1, 10, 96, 16, None) == sa.SA_ERR_SHAPE
+    assert L.sa_sfa_sparsify(P(), P(), 1, 10, 128, -1, None) == sa.SA_ERR_RANGE
+    assert L.sa_sfa_sparsify(P(), P(), 9, 10, 128, 16, None) == sa.SA_ERR_DTYPE
+    assert L.sa_sfa_sparsify(None, P(), 1, 10, 128, 16, None) == sa.SA_ERR_NULL
+    assert L.sa_sfa_sparsify(None, None, 1, 0, 128, 16, None) == sa.SA_OK
 
 
 def test_workspace_sizes():
