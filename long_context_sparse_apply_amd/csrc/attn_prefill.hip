@@ -126,13 +126,20 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Maximum of two scores.  Scores are never NaN, so the NaN-propagating
+// maximum (v_maximum3_f32 on this target) gives the same value as fmaxf
+// without fmaxf's canonicalising of every MFMA result first.
+__device__ __forceinline__ float max_nn(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // Max / sum of a value over lanes l and l ^ 32 (the two key halves of a
 // query) with v_permlane32_swap, which trades the wave's 32-lane halves
 // without an LDS round trip: for lane l < 32 the pair is (x[l], x[l + 32]),
 // for lane l >= 32 it is (x[l - 32], x[l]).
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -221,7 +228,7 @@ __device__ __forceinline__ float chunk_maxval(const f32x16 (&sacc)[2], float sl2
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mblk = fmaxf(mblk, sacc[kt][r]);
+    for (int r = 0; r < 16; ++r) mblk = max_nn(mblk, sacc[kt][r]);
   return pair_max(mblk) * sl2;
 }
 
@@ -301,9 +308,13 @@ __device__ __forceinline__ float chunk_step(const uint8_t* kbuf, const uint8_t* 
     const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * i + 1], sl2, neg_m));
     pw[s][i] = cvt_pk_bf16(p0, p1);
     lsum += p0 + p1;
+    asm volatile("" : "+v"(lsum));  // keep the sum in its slot (see max_unit)
   };
+  // the empty asm keeps each unit in its slot: without it the compiler sinks
+  // the whole max to the end of the step, behind the last MFMA
   auto max_unit = [&](int kt, int m) {
-    mx = fmaxf(mx, fmaxf(snext[kt][2 * m], snext[kt][2 * m + 1]));
+    mx = max_nn(mx, max_nn(snext[kt][2 * m], snext[kt][2 * m + 1]));
+    asm volatile("" : "+v"(mx));
   };
   auto operand = [&](int j) {
     u32x4 t;
