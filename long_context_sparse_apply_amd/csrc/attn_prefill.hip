@@ -306,8 +306,11 @@ __device__ __forceinline__ float chunk_step(const uint8_t* kbuf, const uint8_t* 
     const int s = u >> 2, i = u & 3;
     const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * i], sl2, neg_m));
     const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * i + 1], sl2, neg_m));
-    pw[s][i] = cvt_pk_bf16(p0, p1);
-    lsum += p0 + p1;
+    const uint32_t w = cvt_pk_bf16(p0, p1);
+    pw[s][i] = w;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, lsum, false);
     asm volatile("" : "+v"(lsum));  // keep the sum in its slot (see max_unit)
   };
   // the empty asm keeps each unit in its slot: without it the compiler sinks
