@@ -382,10 +382,18 @@ def cpu_baseline(cfg):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
+    cpu_model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": cfg.B * cfg.S / dt, "unit": "tok/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"the whole 32K prefill layer ({cfg.Hq} query heads, {cfg.S} tokens), "
-                      f"one pass: {dt:.1f} s"}
+                      f"one pass: {dt:.1f} s on {cpu_model}"}
 
 
 def measured_traffic(summary_path, kernel_source):

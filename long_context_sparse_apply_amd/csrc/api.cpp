@@ -254,6 +254,6 @@ const char* sa_status_string(sa_status s) {
   return "unknown status";
 }
 
-int sa_version(void) { return 100; }
+int sa_version(void) { return 200; }
 
 }  // extern "C"
