@@ -253,3 +253,38 @@ def test_decode_full_size_sampled(sa, name, cfg, batches, kv):
         assert p in set(g_idx[b, h, :g_cnt[b, h]].tolist()), (b, h, p)
     del step, dt
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("slab", [0, 1], ids=["std", "slab"])
+def test_decode_degenerate_lengths(sa, slab):
+    """Cache lengths 0, 1 and fewer than k in one batch: an empty cache gives
+    out = 0 and lse = -inf, a single token returns its value row, a short
+    cache keeps every token and matches full attention over it."""
+    import synth.device as SD
+    cfg = W.C4.with_(B=3, Hq=8, Hkv=2, L=700, k=256, slab=slab, needles_per_head=0)
+    say(f"case: decode degenerate lengths slab={slab}")
+    x = W.decode_inputs_host(cfg)
+    dt = SD.decode_tensors(cfg)
+    lens = np.array([0, 1, 200], np.int32)
+    x["lens"] = lens
+    dt["lens"] = torch.from_numpy(lens).to(DEV)
+    step = _decode_step(sa, cfg, x, dt)
+    step.run()
+    torch.cuda.synchronize()
+    cnt = step.tok_cnt.cpu().numpy()
+    idx = step.tok_idx.cpu().numpy()
+    out = _host(step.out)
+    lse = step.lse.cpu().numpy()
+    assert np.all(cnt[0] == 0) and np.all(out[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    assert np.all(cnt[1] == 1) and np.all(idx[1, :, 0] == 0)
+    for h in range(cfg.Hq):
+        assert np.array_equal(out[1, h], x["v"][1, h // cfg.group, 0].astype(np.float64))
+    assert np.all(cnt[2] == 200)
+    assert np.array_equal(idx[2, :, :200], np.tile(np.arange(200), (cfg.Hq, 1)))
+    q_rot = O.decode_query(x["q_raw"].astype(np.float64), lens, cfg.theta)
+    for h in range(cfg.Hq):
+        g = h // cfg.group
+        ro, rl = O.decode_attention(q_rot[2:3, h:h + 1], x["k"][2:3, g:g + 1].astype(np.float64),
+                                    x["v"][2:3, g:g + 1].astype(np.float64),
+                                    [[list(range(200))]], cfg.d ** -0.5)
+        assert np.abs(out[2, h] - ro[0, 0]).max() <= OUT_ATOL[cfg.dtype]
