@@ -288,3 +288,18 @@ def test_decode_degenerate_lengths(sa, slab):
                                     x["v"][2:3, g:g + 1].astype(np.float64),
                                     [[list(range(200))]], cfg.d ** -0.5)
         assert np.abs(out[2, h] - ro[0, 0]).max() <= OUT_ATOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("S", [128, 256], ids=["one-block", "two-blocks"])
+def test_prefill_few_blocks(sa, S):
+    """A layer of one or two blocks: the sink and local windows cover every
+    visible block, so the layer is dense causal attention."""
+    cfg = W.C2.with_(S=S, Hq=8, Hkv=2, needle_pairs=0)
+    say(f"case: prefill {S} tokens")
+    q, k, v, heads = W.prefill_inputs_host(cfg)
+    layer = _layer(sa, cfg, _dev(q, cfg.dtype), _dev(k, cfg.dtype), _dev(v, cfg.dtype))
+    layer.run()
+    torch.cuda.synchronize()
+    cnt = layer.blk_cnt.cpu().numpy()
+    assert np.array_equal(cnt[0, 0], np.arange(1, cfg.N + 1))
+    _compare_prefill(cfg, layer, q, k, v, heads)
