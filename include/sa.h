@@ -125,6 +125,11 @@ sa_status sa_kv_cache_append(const void* k_new, const void* v_new, sa_dtype dtyp
  *   causal: 1 -> scores[.., I, J] = -inf for J > I.
  *   q_rope_out / k_rope_out (nullable): rotated Q / K written in dtype, as
  *   the sparse attention reads them (one pass over Q and K for both).
+ *   q_rope_scale: every stored Q element is the fp32 rotated value times
+ *   this factor, then rounded to dtype (1 -> plain rotated Q).  Passing
+ *   sm_scale * log2(e) here and sm_scale = ln 2 (the float nearest) to
+ *   sa_sparse_attn_prefill gives the same attention with the base-2
+ *   exponent folded into Q.  The pooled vectors and scores never see it.
  *   pooled_q_out [B, Hq, N, d] / pooled_k_out [B, Hkv, N, d] (nullable):
  *   calibrated pooled vectors, fp32.
  *   scores [B, Hq, N, N] fp32:  sm_scale * <pooled_q(h, I), pooled_k(g(h), J)>.
@@ -132,13 +137,15 @@ sa_status sa_kv_cache_append(const void* k_new, const void* v_new, sa_dtype dtyp
  *   NULL; sa_workspace_bytes(SA_OP_BLOCK_SCORE, B*(Hq+Hkv)*N, d, 0, 0, 0)
  *   bytes always suffice (ws may be NULL when both pooled outputs are given).
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_RANGE (split outside [0, d/2],
- *         theta <= 1), SA_ERR_WORKSPACE, SA_ERR_DTYPE.
+ *         theta <= 1, q_rope_scale not finite), SA_ERR_WORKSPACE,
+ *         SA_ERR_DTYPE.
  */
 sa_status sa_block_score(const void* q, const void* k, sa_dtype dtype, int B, int Hq, int Hkv,
                          int S, int d, double theta, int block, int band_split_pair,
                          int calibrate, float sm_scale, int causal, void* q_rope_out,
-                         void* k_rope_out, float* pooled_q_out, float* pooled_k_out,
-                         float* scores, void* ws, size_t ws_bytes, void* stream);
+                         float q_rope_scale, void* k_rope_out, float* pooled_q_out,
+                         float* pooled_k_out, float* scores, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /*
  * sa_token_score -- FASA Token Importance Predictor (sec. 2.B item 1): the
@@ -200,7 +207,11 @@ sa_status sa_topk_select(const float* scores, int64_t rows, int cols, const int3
  *   keys; lse [B, Hq, S] fp32 (nullable) = natural log-sum-exp of the
  *   scaled logits.  A query with no visible key gets out = 0, lse = -inf.
  *   bf16 uses bf16 matrix cores with fp32 accumulation and fp32 softmax;
- *   fp32 computes in fp32 throughout.
+ *   fp32 computes in fp32 throughout.  With bf16 and sm_scale equal to the
+ *   float nearest ln 2, the logits are taken as base-2 exponents directly
+ *   (softmax(ln 2 x) = 2^x / sum 2^x), which saves one multiply-add per
+ *   score: Q pre-multiplied by sm_scale * log2(e) (sa_block_score's
+ *   q_rope_scale) then attends exactly as Q with sm_scale would.
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE (S % block, block not 64/128 for bf16 or
  *         not in {16..256}, d), SA_ERR_RANGE (max_sel < 1), SA_ERR_DTYPE.
  */

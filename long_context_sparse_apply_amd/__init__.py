@@ -45,7 +45,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "sa_rope_apply": [P, P, I, I, I, I, I, P, I, D, P],
         "sa_kv_cache_append": [P, P, I, I, I, I, I, I, P, D, I, P, I, P, P, P, P],
-        "sa_block_score": [P, P, I, I, I, I, I, I, D, I, I, I, F, I, P, P, P, P, P, P, SZ, P],
+        "sa_block_score": [P, P, I, I, I, I, I, I, D, I, I, I, F, I, P, F, P, P, P, P, P, SZ, P],
         "sa_token_score": [P, P, P, I, I, I, I, I, I, P, P, I, I, F, P, P],
         "sa_topk_select": [P, I64, I, P, P, I, I, I, P, I, P, P, SZ, P],
         "sa_sparse_attn_prefill": [P, P, P, I, I, I, I, I, I, I, P, P, I, I, F, P, P, P],
@@ -181,8 +181,12 @@ def sa_kv_cache_append(k_new, v_new, start, k_cache, v_cache, *, theta: float, k
 
 def sa_block_score(q, k, scores, *, theta: float, block: int, band_split_pair: int,
                    calibrate: bool = True, sm_scale: float, causal: bool = True, q_rope_out=None,
-                   k_rope_out=None, pooled_q_out=None, pooled_k_out=None, ws=None, stream=None):
-    """q [B,Hq,S,d], k [B,Hkv,S,d] (raw) -> scores [B,Hq,N,N] fp32."""
+                   q_rope_scale: float = 1.0, k_rope_out=None, pooled_q_out=None,
+                   pooled_k_out=None, ws=None, stream=None):
+    """q [B,Hq,S,d], k [B,Hkv,S,d] (raw) -> scores [B,Hq,N,N] fp32.
+
+    q_rope_out receives the rotated Q times q_rope_scale (rounded to q's dtype).
+    """
     torch = _torch()
     _check(q, "q", ndim=4)
     _check(k, "k", q.dtype, 4)
@@ -196,7 +200,8 @@ def sa_block_score(q, k, scores, *, theta: float, block: int, band_split_pair: i
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _call("sa_block_score", _ptr(q), _ptr(k), _dtype_code(q), B, Hq, Hkv, S, d, float(theta),
           block, band_split_pair, int(bool(calibrate)), float(sm_scale), int(bool(causal)),
-          _ptr(q_rope_out), _ptr(k_rope_out), _ptr(pooled_q_out), _ptr(pooled_k_out),
+          _ptr(q_rope_out), float(q_rope_scale), _ptr(k_rope_out), _ptr(pooled_q_out),
+          _ptr(pooled_k_out),
           _ptr(scores), _ptr(ws), ws_bytes, _stream(stream))
     return scores
 

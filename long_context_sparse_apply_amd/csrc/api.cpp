@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "sa_internal.hpp"
 
 namespace {
@@ -82,14 +84,17 @@ sa_status sa_kv_cache_append(const void* k_new, const void* v_new, sa_dtype dtyp
 sa_status sa_block_score(const void* q, const void* k, sa_dtype dtype, int B, int Hq, int Hkv,
                          int S, int d, double theta, int block, int band_split_pair,
                          int calibrate, float sm_scale, int causal, void* q_rope_out,
-                         void* k_rope_out, float* pooled_q_out, float* pooled_k_out,
-                         float* scores, void* ws, size_t ws_bytes, void* stream) {
+                         float q_rope_scale, void* k_rope_out, float* pooled_q_out,
+                         float* pooled_k_out, float* scores, void* ws, size_t ws_bytes,
+                         void* stream) {
   if (!dtype_ok(dtype)) return SA_ERR_DTYPE;
   if (!q || !k || !scores) return SA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S < 1 || !head_dim_ok(d) ||
       !block_ok(block) || S % block != 0)
     return SA_ERR_SHAPE;
-  if (!(theta > 1.0) || band_split_pair < 0 || band_split_pair > d / 2) return SA_ERR_RANGE;
+  if (!(theta > 1.0) || band_split_pair < 0 || band_split_pair > d / 2 ||
+      !std::isfinite(q_rope_scale))
+    return SA_ERR_RANGE;
   const int N = S / block;
   const size_t pq_bytes = static_cast<size_t>(B) * Hq * N * d * sizeof(float);
   const size_t pk_bytes = static_cast<size_t>(B) * Hkv * N * d * sizeof(float);
@@ -105,7 +110,8 @@ sa_status sa_block_score(const void* q, const void* k, sa_dtype dtype, int B, in
   const sa::RopeFreq fr = sa::make_rope_freq(d, theta);
   hipStream_t st = as_stream(stream);
   hipError_t e = sa::launch_rope_pool(q, k, dtype, B, Hq, Hkv, S, d, block, band_split_pair,
-                                      calibrate ? 1 : 0, fr, q_rope_out, k_rope_out, pq, pk, st);
+                                      calibrate ? 1 : 0, fr, q_rope_out, q_rope_scale, k_rope_out,
+                                      pq, pk, st);
   if (e != hipSuccess) return SA_ERR_HIP;
   return launched(sa::launch_block_gemm(pq, pk, B, Hq, Hkv, N, d, sm_scale, causal ? 1 : 0,
                                         scores, st));

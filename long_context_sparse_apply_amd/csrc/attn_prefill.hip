@@ -24,6 +24,8 @@
 //
 // fp32 path: a plain kernel, one query per LPT = d/8 lanes, online softmax
 // over the selected keys in order, fp32 throughout.
+#include <cmath>
+
 #include "sa_common.hpp"
 
 namespace sa {
@@ -250,6 +252,38 @@ __device__ __forceinline__ void chunk_rescale(SoftmaxState<DT>& st, float mblk, 
   }
 }
 
+// Unit mode (q pre-multiplied by sm_scale * log2 e, so scores are base-2
+// exponents): the S MFMAs start from -m_ref, so the scores come out relative
+// to the reference and p = 2^s needs no further instruction.  The reference
+// lives on the grid of multiples of 64 and moves only when a chunk's max
+// (relative) exceeds 64: then O and l scale by an exact power of two, the
+// pending scores and the -m_ref tile shift by the same multiple of 64, and
+// every p stays <= 2^64 (fp32 and bf16 keep their relative precision).  For
+// ordinary logits the reference stays 0.
+__device__ __forceinline__ float grid64(float m) { return 64.f * rintf(m * (1.f / 64.f)); }
+
+template <int DT>
+__device__ __forceinline__ void chunk_rescale_unit(SoftmaxState<DT>& st, float mrel, bool valid,
+                                                   f32x16 (&snext)[2], f32x16& negm) {
+  const bool raise = valid && mrel > 64.f;
+  if (__ballot(raise)) {
+    const float delta = raise ? grid64(mrel) : 0.f;
+    const float alpha = ldexpf(1.f, -static_cast<int>(delta));  // exact power of two
+    st.l_part *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc_o[dt][r] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      snext[0][r] -= delta;
+      snext[1][r] -= delta;
+      negm[r] -= delta;
+    }
+    st.m_ref += delta;
+  }
+}
+
 // Slot plan of one pipelined step (NS = 2 D/16 S MFMAs, NP = 4 D/32 P V
 // MFMAs, NT = NS + NP slots, one MFMA per slot):
 //   S(c + 1) keys 0-31 | P V k-steps 0, 1 | S(c + 1) keys 32-63 | P V k-steps 2, 3
@@ -290,11 +324,12 @@ struct StepPlan {
 // values.  Returns the max (base 2) of S(c + 1) for this lane's query,
 // before any causal mask (the caller masks a diagonal chunk and takes its max
 // again).
-template <int D>
+template <int D, bool UNIT>
 __device__ __forceinline__ float chunk_step(const uint8_t* kbuf, const uint8_t* vbuf,
                                             const ChunkOffsets<D>& off, const bf16x8 (&qf)[D / 16],
                                             const f32x16 (&sacc)[2], f32x16 (&snext)[2],
-                                            SoftmaxState<D / 32>& st, float sl2) {
+                                            SoftmaxState<D / 32>& st, float sl2,
+                                            const f32x16& negm) {
   using Plan = StepPlan<D>;
   constexpr int ROWB = 2 * D;
   constexpr int DT = Plan::DT, NT = Plan::NT;
@@ -304,8 +339,14 @@ __device__ __forceinline__ float chunk_step(const uint8_t* kbuf, const uint8_t* 
   float mx = -INFINITY;
   auto pword = [&](int u) {
     const int s = u >> 2, i = u & 3;
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * i], sl2, neg_m));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * i + 1], sl2, neg_m));
+    const float x0 = sacc[s >> 1][8 * (s & 1) + 2 * i];
+    const float x1 = sacc[s >> 1][8 * (s & 1) + 2 * i + 1];
+    // unit mode: the scores already are the base-2 exponents (the S MFMAs
+    // start from -m_ref)
+    const float a0 = UNIT ? x0 : fmaf(x0, sl2, neg_m);
+    const float a1 = UNIT ? x1 : fmaf(x1, sl2, neg_m);
+    const float p0 = __builtin_amdgcn_exp2f(a0);
+    const float p1 = __builtin_amdgcn_exp2f(a1);
     const uint32_t w = cvt_pk_bf16(p0, p1);
     pw[s][i] = w;
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -337,7 +378,7 @@ __device__ __forceinline__ float chunk_step(const uint8_t* kbuf, const uint8_t* 
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) snext[kt][r] = 0.f;
+    for (int r = 0; r < 16; ++r) snext[kt][r] = UNIT ? negm[r] : 0.f;
   constexpr int PFD = Plan::PFD;
   u32x4 op[NT];
 #pragma unroll
@@ -365,7 +406,7 @@ __device__ __forceinline__ float chunk_step(const uint8_t* kbuf, const uint8_t* 
     __builtin_amdgcn_sched_barrier(0);
   }
   st.l_part = lsum;
-  return pair_max(mx) * sl2;
+  return UNIT ? pair_max(mx) : pair_max(mx) * sl2;
 }
 
 // The slot plan's promises, checked at compile time: every P word is ready
@@ -404,7 +445,7 @@ static_assert(step_plan_ok<64>() && step_plan_ok<128>(), "prefill step slot plan
 // matrix unit, P(c) and the max of S(c+1) on the vector unit, followed by the
 // causal mask of a diagonal chunk and the lazy rescale.  The loop is unrolled
 // by two so each half names its buffers statically.
-template <int D, int BS>
+template <int D, int BS, bool UNIT>
 __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int B, int Hq, int Hkv, int S, const int32_t* __restrict__ blk_idx,
@@ -471,7 +512,9 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       qf[s] = __builtin_bit_cast(bf16x8, t);
     }
   }
-  const float sl2 = scale * kLog2e;
+  // unit mode: q arrives pre-multiplied by sm_scale * log2(e), so the scores
+  // are already exponents in base 2
+  const float sl2 = UNIT ? 1.f : scale * kLog2e;
   SoftmaxState<DT> st;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -489,6 +532,9 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
 
   ChunkOffsets<D> off;
   off.init(l32, hi, grp16, i16);
+  f32x16 negm;  // unit mode: -m_ref in every slot, the S MFMAs' starting value
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
   f32x16 sacc[2];
   if (t0 < cnt) {
     // prologue: K(0) -> K0; then K(1) -> K1 and V(0) -> V0 while S(0) is computed
@@ -499,7 +545,18 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     Tile::issue(vbase + chunk_row0(t0, c0) * D, sV0, wid, lane);
     chunk_scores<D>(sK0, off, qf, sacc);
     if (causal && sel[t0] == I) chunk_mask(sacc, c0 * 64, qloc, hi);
-    st.m_ref = chunk_maxval(sacc, sl2);  // O and l are still zero: nothing to rescale
+    // O and l are still zero: nothing to rescale
+    st.m_ref = chunk_maxval(sacc, sl2);
+    if (UNIT) {
+      // reference on the 64-grid (0 when no key is visible: every p is then 0)
+      st.m_ref = st.m_ref == -INFINITY ? 0.f : grid64(st.m_ref);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sacc[0][r] -= st.m_ref;
+        sacc[1][r] -= st.m_ref;
+        negm[r] = -st.m_ref;
+      }
+    }
   }
   // One step: chunk c's P and P V with V in vread, chunk c + 1's S with K in
   // kread; K(c + 2) goes to kwrite, V(c + 1) to vwrite.  S(c + 1) is computed
@@ -513,12 +570,13 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     off.pin();
     const bool next = t1 < cnt;
     f32x16 snext[2];
-    float mblk = chunk_step<D>(kread, vread, off, qf, sacc, snext, st, sl2);
+    float mblk = chunk_step<D, UNIT>(kread, vread, off, qf, sacc, snext, st, sl2, negm);
     if (causal && next && sel[t1] == I) {  // uniform: chunk c + 1 is on the diagonal
       chunk_mask(snext, c1 * 64, qloc, hi);
       mblk = chunk_maxval(snext, sl2);
     }
-    chunk_rescale<DT>(st, mblk, next);
+    if (UNIT) chunk_rescale_unit<DT>(st, mblk, next, snext, negm);
+    else chunk_rescale<DT>(st, mblk, next);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) sacc[kt] = snext[kt];
     t0 = t1; c0 = c1;
@@ -630,9 +688,20 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int dtype
     const auto* kk = static_cast<const uint16_t*>(k);
     const auto* vv = static_cast<const uint16_t*>(v);
     auto* oo = static_cast<uint16_t*>(out);
-#define SA_PF(D, BS)                                                                           \
-  prefill_mfma_kernel<D, BS><<<grid, BS * 2, 0, st>>>(qq, kk, vv, B, Hq, Hkv, S, blk_idx, blk_cnt, \
-                                                      max_sel, causal, scale, oo, lse)
+    // sm_scale = ln 2 (the float nearest): the logits are base-2 exponents as
+    // they stand (the caller folded sm_scale * log2 e into q)
+    const bool unit = scale == kLn2;
+#define SA_PF(D, BS)                                                                               \
+  do {                                                                                             \
+    if (unit)                                                                                      \
+      prefill_mfma_kernel<D, BS, true><<<grid, BS * 2, 0, st>>>(qq, kk, vv, B, Hq, Hkv, S, blk_idx, \
+                                                                blk_cnt, max_sel, causal, scale,   \
+                                                                oo, lse);                          \
+    else                                                                                           \
+      prefill_mfma_kernel<D, BS, false><<<grid, BS * 2, 0, st>>>(qq, kk, vv, B, Hq, Hkv, S,        \
+                                                                 blk_idx, blk_cnt, max_sel, causal, \
+                                                                 scale, oo, lse);                  \
+  } while (0)
     if (d == 128) { if (block == 128) SA_PF(128, 128); else SA_PF(128, 64); }
     else { if (block == 128) SA_PF(64, 128); else SA_PF(64, 64); }
 #undef SA_PF

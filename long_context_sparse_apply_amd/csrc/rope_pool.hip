@@ -89,12 +89,13 @@ hipError_t launch_rope(const void* x, void* out, int dtype, int B, int H, int S,
 // row, sums the rotated channels and the per-band squared norms, then forms
 //   m = sum / block,  e_tok = sqrt(E_band / (block |band|)),
 //   e_pool = sqrt(|m_band|^2 / |band|),  pooled = m * e_tok / e_pool.
-// The sums use the fp32 rotated values before any bf16 rounding.
+// The sums use the fp32 rotated values before any bf16 rounding.  Stored
+// query rows are multiplied by q_scale first (the pooled vectors are not).
 template <typename T, int D, int MAXR>
 __global__ __launch_bounds__(256) void rope_pool_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int Hq, int Hkv, int S, int block,
-    int split, int calibrate, RopeFreq fr, T* __restrict__ q_rope, T* __restrict__ k_rope,
-    float* __restrict__ pq, float* __restrict__ pk) {
+    int split, int calibrate, RopeFreq fr, T* __restrict__ q_rope, float q_scale,
+    T* __restrict__ k_rope, float* __restrict__ pq, float* __restrict__ pk) {
   constexpr int P = D / 2;
   constexpr int CH = P / 8;         // threads per token row
   constexpr int RP = 256 / CH;      // rows per pass
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(
     const int h = is_k ? g : g * grp + (hr - 1);
     const int H = is_k ? Hkv : Hq;
     T* dst = is_k ? k_rope : q_rope;
+    const float osc = is_k ? 1.f : q_scale;
     if (dst) dst += ((static_cast<int64_t>(b) * H + h) * S + static_cast<int64_t>(I) * block) * D;
     float* pool_out = (is_k ? pk : pq) + ((static_cast<int64_t>(b) * H + h) * N + I) * D;
     Raw cur_a[MAXR], cur_b[MAXR];
@@ -190,8 +192,11 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(
           if (8 * c + j < split) e_hi += e; else e_lo += e;
         }
         if (dst) {
-          Elem<T>::store8(dst + static_cast<int64_t>(r) * D + 8 * c, ra);
-          Elem<T>::store8(dst + static_cast<int64_t>(r) * D + P + 8 * c, rb);
+          float oa[8], ob[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) { oa[j] = ra[j] * osc; ob[j] = rb[j] * osc; }
+          Elem<T>::store8(dst + static_cast<int64_t>(r) * D + 8 * c, oa);
+          Elem<T>::store8(dst + static_cast<int64_t>(r) * D + P + 8 * c, ob);
         }
       }
     }
@@ -265,7 +270,8 @@ __global__ __launch_bounds__(256) void rope_pool_kernel(
 
 hipError_t launch_rope_pool(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int S,
                             int d, int block, int split, int calibrate, const RopeFreq& fr,
-                            void* q_rope, void* k_rope, float* pq, float* pk, hipStream_t st) {
+                            void* q_rope, float q_scale, void* k_rope, float* pq, float* pk,
+                            hipStream_t st) {
   const dim3 grid(S / block, Hkv, B);
   const int CH = d / 16;
   const int RP = 256 / CH;
@@ -273,7 +279,7 @@ hipError_t launch_rope_pool(const void* q, const void* k, int dtype, int B, int 
 #define SA_RP_LAUNCH(T, D, R)                                                                     \
   rope_pool_kernel<T, D, R><<<grid, 256, 0, st>>>(                                                \
       static_cast<const T*>(q), static_cast<const T*>(k), Hq, Hkv, S, block, split, calibrate, fr, \
-      static_cast<T*>(q_rope), static_cast<T*>(k_rope), pq, pk)
+      static_cast<T*>(q_rope), q_scale, static_cast<T*>(k_rope), pq, pk)
 #define SA_RP_R(T, D)                               \
   if (rows_per_thread <= 1) SA_RP_LAUNCH(T, D, 1);  \
   else if (rows_per_thread <= 2) SA_RP_LAUNCH(T, D, 2); \

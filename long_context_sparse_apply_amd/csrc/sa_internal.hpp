@@ -34,7 +34,8 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, int dtype, int
 // fused rotation + calibrated dual-band block pooling of Q and K (one pass)
 hipError_t launch_rope_pool(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int S,
                             int d, int block, int split, int calibrate, const RopeFreq& fr,
-                            void* q_rope, void* k_rope, float* pq, float* pk, hipStream_t st);
+                            void* q_rope, float q_scale, void* k_rope, float* pq, float* pk,
+                            hipStream_t st);
 
 hipError_t launch_block_gemm(const float* pq, const float* pk, int B, int Hq, int Hkv, int N,
                              int d, float scale, int causal, float* scores, hipStream_t st);

@@ -17,6 +17,9 @@ Decode ("FASA: Frequency-aware Sparse Attention"):
 """
 from __future__ import annotations
 
+import math
+
+import numpy as np
 import torch
 
 from . import (SA_OP_BLOCK_SCORE, SA_OP_DECODE, prefill_row_params, sa_block_score,
@@ -36,6 +39,14 @@ class PrefillLayer:
         self.calibrate, self.causal = calibrate, causal
         self.n_sink, self.n_local = n_sink, n_local
         self.scale = sm_scale if sm_scale is not None else d ** -0.5
+        # bf16: the stored Q carries sm_scale * log2(e) and the attention runs
+        # with sm_scale = ln 2, so its logits are base-2 exponents as they
+        # stand (the same softmax, one multiply-add less per score)
+        if q.dtype == torch.bfloat16:
+            self.q_rope_scale = self.scale * math.log2(math.e)
+            self.attn_scale = float(np.float32(math.log(2.0)))
+        else:
+            self.q_rope_scale, self.attn_scale = 1.0, self.scale
         dev = q.device
         N = self.N
         self.q_rope = torch.empty_like(q)
@@ -62,7 +73,8 @@ class PrefillLayer:
     def score(self):
         sa_block_score(self.q, self.k, self.scores, theta=self.theta, block=self.block,
                        band_split_pair=self.split, calibrate=self.calibrate, sm_scale=self.scale,
-                       causal=self.causal, q_rope_out=self.q_rope, k_rope_out=self.k_rope,
+                       causal=self.causal, q_rope_out=self.q_rope,
+                       q_rope_scale=self.q_rope_scale, k_rope_out=self.k_rope,
                        pooled_q_out=self.pq, pooled_k_out=self.pk, ws=self.ws)
 
     def select(self):
@@ -72,8 +84,8 @@ class PrefillLayer:
 
     def attend(self):
         sa_sparse_attn_prefill(self.q_rope, self.k_rope, self.v, self.blk_idx, self.blk_cnt,
-                               self.out, block=self.block, sm_scale=self.scale, causal=self.causal,
-                               lse=self.lse)
+                               self.out, block=self.block, sm_scale=self.attn_scale,
+                               causal=self.causal, lse=self.lse)
 
     def run(self):
         self.score()

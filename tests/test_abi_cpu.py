@@ -69,13 +69,16 @@ def test_validation_errors_before_launch():
     assert kva(slab=1, dom=P(), n_dom=16) == sa.SA_ERR_NULL   # no k_rest while 2*n_dom < d
     # block score: S % block, Hq % Hkv, split range, workspace
     args = dict(theta=1e4, block=64, split=16)
-    def bs(B=1, Hq=4, Hkv=2, S=512, d=64, block=64, split=16, ws=None, wsb=0, pq=None, pk=None):
+    def bs(B=1, Hq=4, Hkv=2, S=512, d=64, block=64, split=16, ws=None, wsb=0, pq=None, pk=None,
+           qsc=1.0):
         return L.sa_block_score(P(), P(), 0, B, Hq, Hkv, S, d, 1e4, block, split, 1, 0.1, 1,
-                                None, None, pq, pk, P(), ws, wsb, None)
+                                None, qsc, None, pq, pk, P(), ws, wsb, None)
     assert bs(S=500) == sa.SA_ERR_SHAPE
     assert bs(Hq=3) == sa.SA_ERR_SHAPE
     assert bs(block=48) == sa.SA_ERR_SHAPE
     assert bs(split=33) == sa.SA_ERR_RANGE
+    assert bs(qsc=float("inf")) == sa.SA_ERR_RANGE
+    assert bs(qsc=float("nan")) == sa.SA_ERR_RANGE
     assert bs() == sa.SA_ERR_WORKSPACE
     assert bs(ws=P(), wsb=100) == sa.SA_ERR_WORKSPACE
     # topk: shapes, ranges, max_out

@@ -149,6 +149,35 @@ def test_block_score(sa, name, cfg, _):
     assert torch.equal(s2, scores)
 
 
+def test_block_score_q_rope_scale(sa):
+    """q_rope_scale multiplies the stored rotated Q (one bf16 rounding of the
+    fp32 product) and leaves the pooled vectors and the scores unchanged."""
+    cfg = W.C2.with_(S=128 * 6, Hq=4, Hkv=2, needle_pairs=0)
+    say("case: block_score q_rope_scale")
+    q, k, v, _h = W.prefill_inputs_host(cfg)
+    qt, kt = _dev(q, cfg.dtype), _dev(k, cfg.dtype)
+    N, scale = cfg.N, cfg.d ** -0.5
+    c = scale * np.log2(np.e)
+    outs = []
+    for qsc in (1.0, c):
+        scores = torch.empty((cfg.B, cfg.Hq, N, N), dtype=torch.float32, device=DEV)
+        pq = torch.empty((cfg.B, cfg.Hq, N, cfg.d), dtype=torch.float32, device=DEV)
+        pk = torch.empty((cfg.B, cfg.Hkv, N, cfg.d), dtype=torch.float32, device=DEV)
+        qr, kr = torch.empty_like(qt), torch.empty_like(kt)
+        sa.sa_block_score(qt, kt, scores, theta=cfg.theta, block=cfg.block,
+                          band_split_pair=cfg.band_split_pair, calibrate=True, sm_scale=scale,
+                          causal=True, q_rope_out=qr, q_rope_scale=qsc, k_rope_out=kr,
+                          pooled_q_out=pq, pooled_k_out=pk)
+        outs.append((scores, pq, qr, kr))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][3], outs[1][3])
+    q_rot = O.rope(q.astype(np.float64), np.arange(cfg.S), cfg.theta) * c
+    got = _host(outs[1][2])
+    assert np.all(np.abs(got - q_rot) <= 2.0 ** -8 * np.abs(q_rot) + 1e-5)
+
+
 # ----------------------------------------------------------------------------- top-k
 def _tricky_scores(rows, cols, seed):
     g = np.random.default_rng(seed)
@@ -278,6 +307,58 @@ def test_sparse_attn_prefill(sa, case):
     fin = np.isfinite(rlse)
     assert np.array_equal(np.isfinite(gl), fin)
     assert np.abs(gl[fin] - rlse[fin]).max() <= (1e-4 if dtype == "f32" else LSE_ATOL_BF16)
+
+
+UNIT_CASES = [  # name, B, Hq, Hkv, S, d, block, max_sel, causal, empty, logit_gain
+    ("d128-b128-gqa", 1, 8, 2, 2048, 128, 128, 6, True, False, 1.0),
+    ("d128-b128-wide-logits", 1, 4, 1, 2048, 128, 128, 8, True, True, 40.0),
+    ("d128-b64-wide-logits-noncausal", 1, 2, 2, 1024, 128, 64, 6, False, False, 40.0),
+    ("d64-b64-wide-logits", 2, 2, 1, 1024, 64, 64, 5, True, False, 25.0),
+    ("d64-b128-tiny-logits", 1, 2, 2, 1024, 64, 128, 4, True, False, 1e-3),
+]
+
+
+@pytest.mark.parametrize("case", UNIT_CASES, ids=[c[0] for c in UNIT_CASES])
+def test_sparse_attn_prefill_base2(sa, case):
+    """sm_scale = ln 2 (the float nearest): the bf16 kernel takes the logits as
+    base-2 exponents as they stand.  Q holds the folded factor (here
+    logit_gain * d^-1/2 * log2 e, rounded to bf16) and keys grow in size along
+    the sequence, so with a large gain later chunks exceed the running
+    reference by far more than 64 (base 2) and the reference moves several
+    times per row."""
+    name, B, Hq, Hkv, S, d, block, max_sel, causal, empty, gain = case
+    say(f"case: prefill base-2 {name}")
+    N = S // block
+    c = gain * d ** -0.5 * np.log2(np.e)
+    q = synth.round_to_bf16(_stored((B, Hq, S, d), "bf16", 21) * c)
+    ramp = (1.0 + 3.0 * np.arange(S) / S)[None, None, :, None]
+    k = synth.round_to_bf16(_stored((B, Hkv, S, d), "bf16", 22) * ramp)
+    v = _stored((B, Hkv, S, d), "bf16", 23)
+    idx, cnt, sel = _random_selection(B, Hq, N, max_sel, S + Hq + 7, causal, empty)
+    out = torch.empty((B, Hq, S, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    ln2 = float(np.float32(np.log(2.0)))
+    sa.sa_sparse_attn_prefill(_dev(q, "bf16"), _dev(k, "bf16"), _dev(v, "bf16"),
+                              torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV), out,
+                              block=block, sm_scale=ln2, causal=causal, lse=lse)
+    torch.cuda.synchronize()
+    ref, rlse = O.prefill_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                    sel, block, ln2, causal)
+    err = np.abs(_host(out) - ref).max()
+    say(f"  max |out - ref| = {err:.3e}")
+    assert err <= OUT_ATOL["bf16"]
+    gl = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(gl), fin)
+    # Each base-2 logit is an fp32 sum of d exact bf16 products started from
+    # -m_ref, a multiple of 64 with |m_ref| <= A + 32, A = max over keys of
+    # sum_i |q_i k_i|: its error is at most (d + 1) 2^-24 (2 A + 32).  lse
+    # (natural) moves by at most ln 2 times that, on top of the bf16 bound.
+    grp = Hq // Hkv
+    A = np.stack([np.abs(q[:, h]) @ np.abs(k[:, h // grp]).transpose(0, 2, 1) for h in range(Hq)],
+                 axis=1).max(axis=-1)
+    tol = LSE_ATOL_BF16 + np.log(2.0) * (d + 1) * 2.0 ** -24 * (2 * A + 32)
+    assert np.all(np.abs(gl[fin] - rlse[fin]) <= tol[fin])
 
 
 # ----------------------------------------------------------------------------- token scores
