@@ -466,7 +466,9 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  // the wave index, in a scalar register: the tile loads' LDS bases derive
+  // from it and then need no per-step move from a vector register
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int grp16 = lane >> 4;
