@@ -377,12 +377,28 @@ __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
       // 1. the rank-th largest sample (sample index as tie-break); each thread
       //    keeps its samples' keys in registers for the radix levels
       const int seg_stride = ncand / kSegs;
-      uint32_t skey[kSampPerThread];
+      // Sample e sits at fa + (e / seg_len) seg_stride + e % seg_len.  The
+      // thread's samples are e = tid + j kLongThreads: segment and offset
+      // advance by kLongThreads / seg_len and kLongThreads % seg_len a step
+      // (one carry at most, the offset staying below seg_len), so no step
+      // divides.  Every load is issued before any key is formed, and a
+      // sample past nsamp reads column fa instead (its key is dropped), so
+      // the loads need no branch and are all in flight together.
+      const int seg_step = kLongThreads / seg_len, off_step = kLongThreads % seg_len;
+      int seg = tid / seg_len, off = tid % seg_len;
+      float sval[kSampPerThread];
 #pragma unroll
       for (int j = 0; j < kSampPerThread; ++j) {
-        const int e = tid + j * kLongThreads;
-        skey[j] = e < nsamp ? order_key(s[fa + (e / seg_len) * seg_stride + e % seg_len]) : 0u;
+        const bool in = tid + j * kLongThreads < nsamp;
+        sval[j] = s[in ? fa + seg * seg_stride + off : fa];
+        seg += seg_step;
+        off += off_step;
+        if (off >= seg_len) { off -= seg_len; ++seg; }
       }
+      uint32_t skey[kSampPerThread];
+#pragma unroll
+      for (int j = 0; j < kSampPerThread; ++j)
+        skey[j] = tid + j * kLongThreads < nsamp ? order_key(sval[j]) : 0u;
       uint64_t prefix = 0;
       int pbits = 0, need = rank;
       while (true) {
