@@ -79,13 +79,20 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   if (live) {
     const int64_t src = (static_cast<int64_t>(b) * Hkv + g) * S + r;
     const int64_t dst = (static_cast<int64_t>(b) * Hkv + g) * Lmax + st + r;
-    float a[8], bb[8], ra[8], rb[8];
+    // every load (the key row, the value row, the 8 frequencies) is issued
+    // before the rotation uses any of them
+    float a[8], bb[8], ra[8], rb[8], va[8], vb[8];
     Elem<T>::load8(k_new + src * D + 8 * c, a);
     Elem<T>::load8(k_new + src * D + P + 8 * c, bb);
+    Elem<T>::load8(v_new + src * D + 8 * c, va);
+    Elem<T>::load8(v_new + src * D + P + 8 * c, vb);
+    double fj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fj[j] = fr.f[8 * c + j];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float cs, sn;
-      rot_cos_sin(st + r, fr.f[8 * c + j], cs, sn);
+      rot_cos_sin(st + r, fj[j], cs, sn);
       ra[j] = a[j] * cs - bb[j] * sn;
       rb[j] = bb[j] * cs + a[j] * sn;
     }
@@ -99,9 +106,6 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
         s_rows[rl][P + 8 * c + j] = rb[j];
       }
     }
-    float va[8], vb[8];
-    Elem<T>::load8(v_new + src * D + 8 * c, va);
-    Elem<T>::load8(v_new + src * D + P + 8 * c, vb);
     Elem<T>::store8(v_out + dst * D + 8 * c, va);
     Elem<T>::store8(v_out + dst * D + P + 8 * c, vb);
   }

@@ -42,11 +42,15 @@ __global__ __launch_bounds__(256) void rope_kernel(const T* __restrict__ x, T* _
   float a[8], bb[8];
   Elem<T>::load8(src + 8 * c, a);
   Elem<T>::load8(src + P + 8 * c, bb);
+  // the 8 frequencies are read together, before the first rotation
+  double fj[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) fj[j] = fr.f[8 * c + j];
   float ra[8], rb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float cs, sn;
-    rot_cos_sin(p, fr.f[8 * c + j], cs, sn);
+    rot_cos_sin(p, fj[j], cs, sn);
     ra[j] = a[j] * cs - bb[j] * sn;
     rb[j] = bb[j] * cs + a[j] * sn;
   }

@@ -60,6 +60,14 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   row_params(row, cols, valid_len, k_per_row, k_const, n, k);
   const float* s = scores + row * cols;
 
+  // all loads first (a slot past the row reads column 0, which every row
+  // has, and is dropped), so they are in flight together
+  float val[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int idx = j * kWave + lane;
+    val[j] = s[idx < n ? idx : 0];
+  }
   uint32_t key[E];
   uint32_t candm = 0, forcm = 0;
 #pragma unroll
@@ -71,7 +79,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
         forcm |= 1u << j;
       } else {
         candm |= 1u << j;
-        key[j] = order_key(s[idx]);
+        key[j] = order_key(val[j]);
       }
     }
   }
