@@ -133,7 +133,7 @@ constexpr int kMaxCap = 8192;         // largest LDS candidate buffer (64-bit co
 constexpr int kMaxLongCols = 262144;  // longest row (the host rejects longer ones)
 constexpr int kSegs = 64;             // sample segments per row
 constexpr int kSegLen = 256;          // samples per segment (at most)
-constexpr int kCollectVec = 8;        // float4 loads a thread per batch of the collect pass
+constexpr int kCollectVec = 4;        // float4 loads a thread per batch of the collect pass
 constexpr int kSampPerThread = kSegs * kSegLen / kLongThreads;
 
 // exclusive prefix sum over the work-group; returns the prefix, sets total
@@ -450,40 +450,79 @@ __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
         const uint64_t c[4] = {composite(order_key(v), i), 0, 0, 0};
         append4(sh, ok, c);
       }
-      // vectorised body, software-pipelined: the next batch of float4 loads is
-      // in flight while the current one is tested
+      // Vectorised body, software-pipelined over four named batches of
+      // kCollectVec float4 a thread: a batch's loads are issued three batches
+      // before it is tested, and no register is copied between batches (a
+      // copy would wait for the loads just issued).  The loads take no branch:
+      // an index at or past a1 reads column a0 instead (a valid aligned
+      // address; a1 > a0 inside the loop) and the value is dropped by the
+      // i < a1 test, so the counter waits stay exact.
       constexpr int kStep = 4 * kLongThreads * kCollectVec;
-      float4 cur[kCollectVec];
-      auto load_batch = [&](float4 (&dst)[kCollectVec], int base) {
+      auto load_batch = [&](float4 (&dst)[kCollectVec], int bbase) {
 #pragma unroll
         for (int u = 0; u < kCollectVec; ++u) {
-          const int i = base + (u * kLongThreads + tid) * 4;
-          dst[u] = i < a1 ? *reinterpret_cast<const float4*>(s + i)
-                          : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          const int i = bbase + (u * kLongThreads + tid) * 4;
+          dst[u] = *reinterpret_cast<const float4*>(s + (i < a1 ? i : a0));
         }
       };
-      if (a0 < a1) load_batch(cur, a0);
-      for (int base = a0; base < a1; base += kStep) {
-        float4 nxt[kCollectVec];
-        if (base + kStep < a1) load_batch(nxt, base + kStep);
+      // the wave's qualifying values of a batch take one LDS atomic for their
+      // slots (lane 0's, broadcast by readfirstlane: every lane is active
+      // here); a value's slot is the running total plus its rank among the
+      // lanes below in its ballot.  Each lane keeps its own qualifying bits
+      // and the ballots are taken again when writing, so only one is live at
+      // a time.
+      auto test_batch = [&](const float4 (&src)[kCollectVec], int bbase) {
+        static_assert(4 * kCollectVec <= 32, "one bit a value of the batch");
+        uint32_t qbits = 0;
+        int tot = 0;
 #pragma unroll
         for (int u = 0; u < kCollectVec; ++u) {
-          const int i = base + (u * kLongThreads + tid) * 4;
-          const float vv[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
-          bool ok[4];
-          bool any = false;
+          const int i = bbase + (u * kLongThreads + tid) * 4;  // i < a1 covers i + 3 (a1 % 4 == 0)
+          const float vv[4] = {src[u].x, src[u].y, src[u].z, src[u].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            ok[e] = i < a1 && qualifies(vv[e]);
-            any |= ok[e];
+            const bool ok = i < a1 && qualifies(vv[e]);
+            qbits |= static_cast<uint32_t>(ok) << (4 * u + e);
+            tot += __popcll(__ballot(ok));
           }
-          if (__ballot(any) == 0) continue;  // the common case: nothing here qualifies
-          const uint64_t c[4] = {composite(order_key(vv[0]), i), composite(order_key(vv[1]), i + 1),
-                                 composite(order_key(vv[2]), i + 2), composite(order_key(vv[3]), i + 3)};
-          append4(sh, ok, c);
         }
+        if (tot == 0) return;
+        const int lane = tid & (kWave - 1);
+        int slot = 0;
+        if (lane == 0) slot = atomicAdd(sh.nbuf, tot);
+        slot = __builtin_amdgcn_readfirstlane(slot);
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
-        for (int u = 0; u < kCollectVec; ++u) cur[u] = nxt[u];
+        for (int u = 0; u < kCollectVec; ++u) {
+          const int i = bbase + (u * kLongThreads + tid) * 4;
+          const float vv[4] = {src[u].x, src[u].y, src[u].z, src[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = (qbits >> (4 * u + e)) & 1u;
+            const uint64_t m = __ballot(ok);
+            if (ok) {
+              const int pos = slot + __popcll(m & below);
+              if (pos < sh.cap) sh.cbuf[pos] = composite(order_key(vv[e]), i + e);
+            }
+            slot += __popcll(m);
+          }
+        }
+      };
+      if (a0 < a1) {
+        float4 b0[kCollectVec], b1[kCollectVec], b2[kCollectVec], b3[kCollectVec];
+        load_batch(b0, a0);
+        load_batch(b1, a0 + kStep);
+        load_batch(b2, a0 + 2 * kStep);
+        for (int base = a0; base < a1; base += 4 * kStep) {
+          load_batch(b3, base + 3 * kStep);
+          test_batch(b0, base);
+          load_batch(b0, base + 4 * kStep);
+          test_batch(b1, base + kStep);
+          load_batch(b1, base + 5 * kStep);
+          test_batch(b2, base + 2 * kStep);
+          load_batch(b2, base + 6 * kStep);
+          test_batch(b3, base + 3 * kStep);
+        }
       }
       for (int i = (a1 > a0 ? a1 : a0) + tid; i < fb; i += kLongThreads) {
         const float v = s[i];
