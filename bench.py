@@ -124,6 +124,9 @@ def time_prefill(layer, steps, warmup, torch, flush):
 
 
 def time_decode(step, steps, warmup, torch, flush):
+    """Per-stage HIP-event times of the decode step.  A fused step (slab
+    layout: one sa_token_topk call scores and selects) has no score / select
+    split: score_us and select_us are None and score_select_us covers both."""
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
@@ -134,18 +137,27 @@ def time_decode(step, steps, warmup, torch, flush):
         e[0].record()
         step.rope()
         e[1].record()
-        step.score()
-        e[2].record()
-        step.select()
+        if step.fused:
+            step.score_select()
+            e[2].record()
+        else:
+            step.score()
+            e[2].record()
+            step.select()
         e[3].record()
         step.attend()
         e[4].record()
     torch.cuda.synchronize()
     parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev]) * 1e3
     total = np.array([e[0].elapsed_time(e[4]) for e in ev]) * 1e3
-    r = dict(attend_us_mean=float(parts[:, 3].mean()))
-    for name, col in (("step_us", total), ("rope_us", parts[:, 0]), ("score_us", parts[:, 1]),
-                      ("select_us", parts[:, 2]), ("attend_us", parts[:, 3])):
+    r = dict(attend_us_mean=float(parts[:, 3].mean()), fused=bool(step.fused))
+    cols = [("step_us", total), ("rope_us", parts[:, 0]), ("attend_us", parts[:, 3]),
+            ("score_select_us", parts[:, 1] + parts[:, 2])]
+    if not step.fused:
+        cols += [("score_us", parts[:, 1]), ("select_us", parts[:, 2])]
+    else:
+        r["score_us"] = r["select_us"] = None
+    for name, col in cols:
         r[name], r[name + "_p10"], r[name + "_p90"] = _stats(col)
     return r
 
@@ -356,9 +368,30 @@ def run_decode(cfg, steps, warmup, torch, flush):
     t["attend_gather_bytes_dedup_per_kv_head"] = decode_dedup_bytes(step.tok_idx.cpu().numpy(), cnt,
                                                                     cfg.Hkv, cfg.d)
     row = 2 * cfg.n_dom if cfg.slab else cfg.d
-    scan = float(cfg.B) * cfg.Hkv * cfg.L * row * 2 + float(cfg.B) * cfg.Hq * cfg.L * 4
-    t["score_bytes"] = scan
-    t["score_hbm_frac"] = scan / (t["score_us"] * 1e-6) / PEAK_HBM_BPS
+    key_bytes = float(cfg.B) * cfg.Hkv * cfg.L * row * 2
+    if step.fused:
+        # the fused top-k reads the key rows once and writes no scores; its
+        # fraction is over the whole score + select time
+        t["score_bytes"] = key_bytes
+        t["score_hbm_frac"] = key_bytes / (t["score_select_us"] * 1e-6) / PEAK_HBM_BPS
+        # the two calls it replaces, on the same inputs, for comparison
+        two = DecodeStep(dt["q_raw"], dt["k"], dt["v"], dt["lens"], dt["dom"], theta=cfg.theta,
+                         top_k=cfg.k, slab=True, k_rest=dt["k_rest"], fused=False)
+        two.rope()
+
+        def score_then_select():
+            two.score()
+            two.select()
+        t["two_step_score_select_us"] = time_call(score_then_select, max(3, steps // 2), 1, torch,
+                                                  flush)[0]
+        torch.cuda.synchronize()
+        t["two_step_equal"] = bool(torch.equal(two.tok_idx, step.tok_idx)
+                                   and torch.equal(two.tok_cnt, step.tok_cnt))
+        del two
+    else:
+        scan = key_bytes + float(cfg.B) * cfg.Hq * cfg.L * 4  # key rows read, scores written
+        t["score_bytes"] = scan
+        t["score_hbm_frac"] = scan / (t["score_us"] * 1e-6) / PEAK_HBM_BPS
     del step, dt
     torch.cuda.empty_cache()
     return t
@@ -475,13 +508,18 @@ def main():
             log(json.dumps(rd))
             secondary[name] = {"us_per_step": rd["step_us"],
                                "us_per_step_p10_p90": [rd["step_us_p10"], rd["step_us_p90"]],
-                               "rope_us": rd["rope_us"], "score_us": rd["score_us"],
+                               "rope_us": rd["rope_us"], "fused_score_select": rd["fused"],
+                               "score_select_us": rd["score_select_us"],
+                               "score_us": rd["score_us"],
                                "select_us": rd["select_us"], "attend_us": rd["attend_us"],
                                "attend_hbm_frac": rd["attend_hbm_frac"],
                                "attend_gather_bytes": rd["attend_gather_bytes"],
                                "attend_gather_bytes_dedup_per_kv_head":
                                    rd["attend_gather_bytes_dedup_per_kv_head"],
                                "score_hbm_frac": rd["score_hbm_frac"]}
+            if rd["fused"]:
+                secondary[name]["two_step_score_select_us"] = rd["two_step_score_select_us"]
+                secondary[name]["two_step_equal"] = rd["two_step_equal"]
         log("decode_64k_slab_host_rest (FASA-M placement)")
         cfg_m = W.C5.with_(B=16, L=65536, k=2048)
         rm = run_decode_host_rest(cfg_m, max(2, args.steps // 5), 1, torch, flush)
@@ -489,8 +527,8 @@ def main():
         secondary["decode_64k_slab_host_rest"] = {
             "workload": "batch 16, KV length 65536, dominant slab (16 pairs) in HBM, "
                         "rest of K and V in pinned host memory, top-2048, bf16",
-            "us_per_step": rm["step_us"], "score_us": rm["score_us"],
-            "select_us": rm["select_us"], "attend_us": rm["attend_us"],
+            "us_per_step": rm["step_us"], "score_select_us": rm["score_select_us"],
+            "attend_us": rm["attend_us"],
             "host_link_bytes": rm["host_link_bytes"], "host_link_GBps": rm["host_link_GBps"],
             "device_resident_bytes": rm["device_resident_bytes"],
             "host_resident_bytes": rm["host_resident_bytes"]}

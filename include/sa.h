@@ -59,7 +59,7 @@ typedef enum {
 typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
 
 /* operation ids for sa_workspace_bytes */
-enum { SA_OP_BLOCK_SCORE = 1, SA_OP_TOPK = 2, SA_OP_DECODE = 3 };
+enum { SA_OP_BLOCK_SCORE = 1, SA_OP_TOPK = 2, SA_OP_DECODE = 3, SA_OP_TOKEN_TOPK = 4 };
 
 /*
  * sa_rope_apply -- rotary position encoding at absolute positions.
@@ -170,6 +170,38 @@ sa_status sa_token_score(const void* q_rope, const void* k, const void* k_rest, 
                          int B, int Hq, int Hkv, int Lmax, int d, const int32_t* cache_len,
                          const int32_t* dom_pairs, int n_dom, int slab, float sm_scale,
                          float* scores, void* stream);
+
+/*
+ * sa_token_topk -- FASA Token Importance Predictor and the critical token
+ * subset in one call (sec. 2.B items 1 and 2), for the dominant-slab cache
+ * layout (sec. 2.C), without writing the score array.
+ *   The result equals, bit for bit, sa_token_score(q_rope, k_dom, NULL, dtype,
+ *   B, Hq, Hkv, Lmax, d, cache_len, dom_pairs, n_dom, slab = 1, sm_scale,
+ *   scores) followed by sa_topk_select(scores, B*Hq, Lmax, valid_len = row
+ *   b*Hq + h -> cache_len[b], k_per_row = NULL, k_const = k_top, n_sink = 0,
+ *   n_local = 0, idx_out, max_out, count_out).
+ *   q_rope [B, Hq, d]; k_dom [B, Hkv, Lmax, 2*n_dom] (the slab); cache_len,
+ *   dom_pairs as in sa_token_score.  2*n_dom channels of dtype must take 16,
+ *   32, 64 or 128 bytes (SA_ERR_UNSUPPORTED otherwise).
+ *   idx_out [B*Hq, max_out] int32 (max_out >= k_top), count_out [B*Hq].
+ *   ws: sa_workspace_bytes(SA_OP_TOKEN_TOPK, B*Hq, Lmax, 0, 0, 0) bytes: per
+ *   row a sampled threshold, and per row, tile of 4096 tokens and scoring
+ *   wave (4 a tile) a candidate count and up to 256 candidates of 8 bytes
+ *   (about 8 KiB per row and 4096 tokens).
+ *   A row's candidates are the tokens whose scores reach its sampled
+ *   threshold; when their number falls outside [k_top, 2*k_top + 1024] (at
+ *   most 8192) or a list overflows, the row's selection reads all its tokens
+ *   again, with their scores recomputed by the same arithmetic, so the
+ *   result never depends on the sample.
+ * Errors: SA_ERR_NULL, SA_ERR_SHAPE (Lmax outside [1, 262144], d, Hq % Hkv),
+ *         SA_ERR_RANGE (n_dom, k_top < 0, max_out < k_top), SA_ERR_WORKSPACE,
+ *         SA_ERR_UNSUPPORTED (Hq / Hkv not 1, 2, 4, 8; slab width), SA_ERR_DTYPE.
+ */
+sa_status sa_token_topk(const void* q_rope, const void* k_dom, sa_dtype dtype, int B, int Hq,
+                        int Hkv, int Lmax, int d, const int32_t* cache_len,
+                        const int32_t* dom_pairs, int n_dom, float sm_scale, int k_top,
+                        int32_t* idx_out, int max_out, int32_t* count_out, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /*
  * sa_topk_select -- per-row selection (Prism sec. 1: keep a subset of
@@ -309,6 +341,8 @@ size_t sa_calibrate_workspace_bytes(int Hq, int Hkv, int M, int L, int d, int k_
  *       cols = d -> scratch for the pooled Q and K vectors.
  *   SA_OP_TOPK: rows, cols -> 0 (reserved).
  *   SA_OP_DECODE: B, Hq, max_k -> split-K partials (sized for d <= 128).
+ *   SA_OP_TOKEN_TOPK: rows = B*Hq, cols = Lmax -> thresholds, counts and
+ *   candidate lists of sa_token_topk.
  * Returns 0 for an unknown op.
  */
 size_t sa_workspace_bytes(int op, int64_t rows, int cols, int B, int Hq, int max_k);

@@ -21,10 +21,10 @@ LIB_PATH = os.path.join(HERE, "libsa_mi355x.so")
 SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_RANGE, SA_ERR_WORKSPACE, \
     SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_ACCESS = range(9)
 SA_F32, SA_BF16 = 0, 1
-SA_OP_BLOCK_SCORE, SA_OP_TOPK, SA_OP_DECODE = 1, 2, 3
+SA_OP_BLOCK_SCORE, SA_OP_TOPK, SA_OP_DECODE, SA_OP_TOKEN_TOPK = 1, 2, 3, 4
 
 EXPORTED = ("sa_rope_apply", "sa_kv_cache_append", "sa_block_score", "sa_token_score",
-            "sa_topk_select", "sa_sparse_attn_prefill", "sa_sparse_attn_decode",
+            "sa_token_topk", "sa_topk_select", "sa_sparse_attn_prefill", "sa_sparse_attn_decode",
             "sa_calibrate_dominant", "sa_calibrate_workspace_bytes", "sa_sfa_sparsify",
             "sa_workspace_bytes",
             "sa_status_string", "sa_version")
@@ -47,6 +47,7 @@ def _load() -> ctypes.CDLL:
         "sa_kv_cache_append": [P, P, I, I, I, I, I, I, P, D, I, P, I, P, P, P, P],
         "sa_block_score": [P, P, I, I, I, I, I, I, D, I, I, I, F, I, P, F, P, P, P, P, P, SZ, P],
         "sa_token_score": [P, P, P, I, I, I, I, I, I, P, P, I, I, F, P, P],
+        "sa_token_topk": [P, P, I, I, I, I, I, I, P, P, I, F, I, P, I, P, P, SZ, P],
         "sa_topk_select": [P, I64, I, P, P, I, I, I, P, I, P, P, SZ, P],
         "sa_sparse_attn_prefill": [P, P, P, I, I, I, I, I, I, I, P, P, I, I, F, P, P, P],
         "sa_sparse_attn_decode": [P, P, P, P, I, I, I, I, I, I, P, P, I, I, P, P, I, F, P, P, P,
@@ -222,6 +223,34 @@ def sa_token_score(q_rope, k, scores, cache_len, dom_pairs, *, sm_scale: float, 
           Lmax, dd, _ptr(cache_len), _ptr(dom_pairs), n_dom, int(bool(slab)), float(sm_scale),
           _ptr(scores), _stream(stream))
     return scores
+
+
+def sa_token_topk(q_rope, k_dom, cache_len, dom_pairs, idx_out, count_out, ws, *, sm_scale: float,
+                  k_top: int, stream=None):
+    """Token scores from the dominant slab and their top-k per (b, h) row in one
+    call, without a score array: q_rope [B,Hq,d], k_dom [B,Hkv,Lmax,2*n_dom] ->
+    idx_out [B,Hq,max_out] (max_out >= k_top), count_out [B,Hq].  ws: uint8 of
+    workspace_bytes(SA_OP_TOKEN_TOPK, rows=B*Hq, cols=Lmax, max_k=k_top)."""
+    torch = _torch()
+    _check(q_rope, "q_rope", ndim=3)
+    _check(k_dom, "k_dom", q_rope.dtype, 4)
+    _check(cache_len, "cache_len", torch.int32, 1)
+    _check(dom_pairs, "dom_pairs", torch.int32, 2)
+    _check(idx_out, "idx_out", torch.int32)
+    _check(count_out, "count_out", torch.int32)
+    if ws is None:
+        raise ValueError("sa_token_topk needs its workspace")
+    _check(ws, "ws")
+    B, Hq, dd = q_rope.shape
+    Hkv, Lmax = k_dom.shape[1], k_dom.shape[2]
+    n_dom = dom_pairs.shape[1]
+    max_out = idx_out.shape[-1]
+    if idx_out.numel() != B * Hq * max_out or count_out.numel() != B * Hq:
+        raise ValueError("idx_out / count_out do not match the (b, h) rows")
+    _call("sa_token_topk", _ptr(q_rope), _ptr(k_dom), _dtype_code(q_rope), B, Hq, Hkv, Lmax, dd,
+          _ptr(cache_len), _ptr(dom_pairs), n_dom, float(sm_scale), int(k_top), _ptr(idx_out),
+          max_out, _ptr(count_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    return idx_out, count_out
 
 
 def sa_topk_select(scores, idx_out, count_out, *, k_const: int, valid_len=None, k_per_row=None,

@@ -19,6 +19,8 @@
 // standard layout, 16-byte reads of the slab) and takes the query slices,
 // staged once per work-group in LDS, as broadcast reads.
 #include "sa_common.hpp"
+#include "token_dot.hpp"
+#include "topk_keys.hpp"
 
 namespace sa {
 
@@ -51,11 +53,16 @@ struct TokenScoreShape {
   static_assert(LPW * 4096 == CHB, "chunk must split over 4 waves");
 };
 
-template <typename T, int ROW, int GRP, int NDC, bool SLAB>
+// COLLECT: instead of storing the scores, append each token whose score
+// passes its row's threshold key (and lies below cache_len) to the wave's own
+// candidate list of that row and tile (blockIdx.x); the wave counts in
+// registers and writes its counts at the end (entries past the slots are
+// dropped, the count stays true).
+template <typename T, int ROW, int GRP, int NDC, bool SLAB, bool COLLECT>
 __global__ __launch_bounds__(256) void token_score_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int Hq, int Hkv, int Lmax, int d,
     const int32_t* __restrict__ cache_len, const int32_t* __restrict__ dom, int n_dom,
-    float scale, float* __restrict__ scores, int chunks_per_wg) {
+    float scale, float* __restrict__ scores, int chunks_per_wg, TokenCollect col) {
   using Sh = TokenScoreShape<T, ROW, GRP, NDC>;
   constexpr int ES = Sh::ES, ROWB = Sh::ROWB, CPR = Sh::CPR, CT = Sh::CT, HPT = Sh::HPT;
   constexpr int CHB = Sh::CHB, LPW = Sh::LPW;
@@ -64,6 +71,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t sk1[CHB];
   __shared__ __attribute__((aligned(16))) float s_q[GRP][NDC];
   __shared__ int s_off[NDC];
+  __shared__ uint32_t s_thr[GRP];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -106,12 +114,18 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     }
     s_q[hh][j] = v;
   }
+  if (COLLECT && tid < GRP) s_thr[tid] = col.thr[static_cast<int64_t>(b) * Hq + g * GRP + tid];
   if (tid < NDC) {
     int c = 0;
     if (tid < ndc) c = SLAB ? tid : (dom[g * n_dom + (tid % n_dom)] + (tid >= n_dom ? P : 0)) & (d - 1);
     s_off[tid] = c * ES;  // byte offset of the channel within an unswizzled row
   }
 
+  static_assert(!COLLECT || (CT == 256 && Sh::HGS0 == 1),
+                "collect mode: every thread scores all heads of its token, one 64-token share a wave");
+  int wcnt[HPT];  // collect mode: this wave's candidates a head so far (equal over the wave)
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) wcnt[u] = 0;
   const int r = tid % CT;              // this thread's token within a chunk
   const int hg = tid / CT;             // its head group (HGS groups of HPT heads)
   const bool active = hg * HPT < GRP;
@@ -146,17 +160,21 @@ __global__ __launch_bounds__(256) void token_score_kernel(
 #pragma unroll
     for (int u = 0; u < HPT; ++u) {
       const int hh = hg * HPT + u;
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < NDC; j += 4) {
-        const float4 qv = *reinterpret_cast<const float4*>(&s_q[hh][j]);
-        acc = fmaf(qv.x, kv[j], acc);
-        acc = fmaf(qv.y, kv[j + 1], acc);
-        acc = fmaf(qv.z, kv[j + 2], acc);
-        acc = fmaf(qv.w, kv[j + 3], acc);
+      const float acc = token_dot<NDC>(&s_q[hh][0], kv);
+      const int64_t srow = static_cast<int64_t>(b) * Hq + g * GRP + hh;
+      if constexpr (COLLECT) {
+        // (t < Lmax too: the selection's row length is cache_len clamped to Lmax)
+        const bool ok = t < L && t < Lmax && KeyThreshold(s_thr[hh]).qualifies(acc);
+        const uint64_t m = __ballot(ok);
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+        const int pos = wcnt[u] + __popcll(m & below);
+        if (ok && pos < kCollectSlots)
+          col.cand[((srow * col.tiles + blockIdx.x) * kCollectWaves + wid) * kCollectSlots + pos] =
+              composite(order_key(acc), t);
+        wcnt[u] += __popcll(m);
+      } else {
+        if (t < Lmax) scores[srow * Lmax + t] = (t < L) ? acc : -INFINITY;
       }
-      if (t < Lmax)
-        scores[(static_cast<int64_t>(b) * Hq + g * GRP + hh) * Lmax + t] = (t < L) ? acc : -INFINITY;
     }
   };
 
@@ -173,11 +191,25 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     if (c + 2 < nch) issue(c + 2, sk0);
     score_chunk(c + 1, sk1);
   }
+
+  // collect mode: the wave's counts of this tile, one a head
+  if constexpr (COLLECT) {
+    if (active && lane == 0) {
+#pragma unroll
+      for (int u = 0; u < HPT; ++u)
+        col.cnt[((static_cast<int64_t>(b) * Hq + g * GRP + hg * HPT + u) * col.tiles + blockIdx.x) *
+                    kCollectWaves + wid] = wcnt[u];
+    }
+  }
 }
 
-hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
-                              int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
-                              int n_dom, int slab, float scale, float* scores, hipStream_t st) {
+// Scoring (COLLECT false: every score into `scores`) or candidate collection
+// for the fused token top-k (COLLECT true, slab layout only).
+template <bool COLLECT>
+static hipError_t launch_scoring(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
+                                 int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
+                                 int n_dom, int slab, float scale, float* scores,
+                                 const TokenCollect& col, hipStream_t st) {
   const int row = slab ? 2 * n_dom : d;
   const int grp = Hq / Hkv;
   const int ndc_need = 2 * n_dom;
@@ -188,12 +220,21 @@ hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, in
   // about 4096 tokens per work-group, fewer when that leaves under ~2048 work-groups
   const int per_head_chunks = (Lmax + ct - 1) / ct;
   int cpw = 4096 / ct;
-  while (cpw > 1 && static_cast<int64_t>(B) * Hkv * ((per_head_chunks + cpw - 1) / cpw) < 2048) cpw /= 2;
+  // (collect mode keeps tiles of kCollectTile tokens: its lists are laid out per tile)
+  while (!COLLECT && cpw > 1 &&
+         static_cast<int64_t>(B) * Hkv * ((per_head_chunks + cpw - 1) / cpw) < 2048)
+    cpw /= 2;
+  if (COLLECT && cpw * ct != kCollectTile) return hipErrorInvalidValue;
   const dim3 grid((per_head_chunks + cpw - 1) / cpw, Hkv, B);
-#define SA_TS(T, R, G, C, SL)                                                                 \
-  token_score_kernel<T, R, G, C, SL><<<grid, 256, 0, st>>>(static_cast<const T*>(q),            \
-                                                           static_cast<const T*>(k), Hq, Hkv, Lmax, \
-                                                           d, cache_len, dom, n_dom, scale, scores, cpw)
+// (collect mode exists for slab rows of at most 128 bytes)
+#define SA_TS(T, R, G, C, SL)                                                                    \
+  if constexpr (!COLLECT || R * sizeof(T) <= 128) {                                              \
+    token_score_kernel<T, R, G, C, SL, COLLECT><<<grid, 256, 0, st>>>(                            \
+        static_cast<const T*>(q), static_cast<const T*>(k), Hq, Hkv, Lmax, d, cache_len, dom,     \
+        n_dom, scale, scores, cpw, col);                                                         \
+  } else {                                                                                       \
+    return hipErrorInvalidValue;                                                                 \
+  }
 #define SA_TS_G(T, R, C, SL)                  \
   switch (grp) {                              \
     case 1: SA_TS(T, R, 1, C, SL); break;     \
@@ -220,6 +261,8 @@ hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, in
       case 128: SA_TS_G(T, 128, 128, true) break;                      \
       default: return hipErrorInvalidValue;                            \
     }                                                                  \
+  } else if constexpr (COLLECT) {                                      \
+    return hipErrorInvalidValue;                                       \
   } else if (d == 128) {                                               \
     SA_TS_STD(T, 128)                                                  \
   } else {                                                             \
@@ -236,6 +279,20 @@ hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, in
 #undef SA_TS_G
 #undef SA_TS
   return hipGetLastError();
+}
+
+hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
+                              int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
+                              int n_dom, int slab, float scale, float* scores, hipStream_t st) {
+  return launch_scoring<false>(q, k, dtype, B, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, slab, scale,
+                               scores, TokenCollect{}, st);
+}
+
+hipError_t launch_token_collect(const void* q, const void* k_dom, int dtype, int B, int Hq, int Hkv,
+                                int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
+                                int n_dom, float scale, const TokenCollect& col, hipStream_t st) {
+  return launch_scoring<true>(q, k_dom, dtype, B, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, 1, scale,
+                              nullptr, col, st);
 }
 
 }  // namespace sa

@@ -27,16 +27,10 @@
 // bitmap is finally compacted into ascending column indices.  The LDS is
 // sized per launch from the row length and k, so two rows of the decode
 // workloads share a CU.
-#include "sa_common.hpp"
+#include "token_dot.hpp"
+#include "topk_keys.hpp"
 
 namespace sa {
-
-__device__ __forceinline__ uint32_t order_key(float s) {
-  uint32_t u = __float_as_uint(s);
-  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;  // NaN ranks as -inf
-  if ((u & 0x7fffffffu) == 0u) u = 0u;                   // -0 equals +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);     // candidates: key >= 0x007fffff
-}
 
 __device__ __forceinline__ void row_params(int64_t row, int cols, const int32_t* valid_len,
                                            const int32_t* k_per_row, int k_const, int& n, int& k) {
@@ -165,13 +159,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& total) {
   return base + x - v;
 }
 
-__device__ __forceinline__ uint64_t composite(uint32_t key, int idx) {
-  return (static_cast<uint64_t>(key) << 32) | static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(idx));
-}
-__device__ __forceinline__ int comp_col(uint64_t c) {
-  return static_cast<int>(0xffffffffu - static_cast<uint32_t>(c & 0xffffffffu));
-}
-
 // Views into the work-group's dynamic LDS: the candidate buffer (cap 64-bit
 // composites), the radix histogram, the selection bitmap (one bit a column)
 // and a few scalars.  Sized per launch from the row length and k.
@@ -270,9 +257,11 @@ __device__ void select_in_lds(const TopkShared& sh, int nbuf, int need) {
   }
 }
 
-// Fallback: radix select reading the row from memory at each level, moving
+// Fallback: radix select over the columns [fa, fb) whose scores `val(i)`
+// gives (read from the row, or recomputed), taken again at each level, moving
 // to the LDS buffer once the undecided values fit (always exact).
-__device__ void select_from_row(const TopkShared& sh, const float* s, int fa, int fb, int need) {
+template <typename Val>
+__device__ void select_from_source(const TopkShared& sh, Val val, int fa, int fb, int need) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0;
   int pbits = 0;
@@ -281,14 +270,14 @@ __device__ void select_from_row(const TopkShared& sh, const float* s, int fa, in
   while (true) {
     int bsel, above, cntb;
     auto each = [&](auto f) {
-      for (int i = fa + tid; i < fb; i += kLongThreads) f(composite(order_key(s[i]), i));
+      for (int i = fa + tid; i < fb; i += kLongThreads) f(composite(order_key(val(i)), i));
     };
     radix_level(sh, pbits, prefix, need, each, bsel, above, cntb);
     need -= above;
     const bool done = (cntb == need);
     const bool collect = !done && cntb <= sh.cap;
     for (int i = fa + tid; i < fb; i += kLongThreads) {
-      const uint64_t c = composite(order_key(s[i]), i);
+      const uint64_t c = composite(order_key(val(i)), i);
       if (pbits != 0 && (c >> (64 - pbits)) != prefix) continue;
       const int dg = static_cast<int>((c << pbits) >> (64 - kDigit));
       if (dg > bsel || (done && dg == bsel)) {
@@ -308,6 +297,10 @@ __device__ void select_from_row(const TopkShared& sh, const float* s, int fa, in
     prefix = (prefix << kDigit) | static_cast<uint64_t>(bsel);
     pbits += kDigit;
   }
+}
+
+__device__ void select_from_row(const TopkShared& sh, const float* s, int fa, int fb, int need) {
+  select_from_source(sh, [s](int i) { return s[i]; }, fa, fb, need);
 }
 
 // Wave-aggregated append of up to four composites a lane (where ok[e]) to the
@@ -335,6 +328,77 @@ __device__ __forceinline__ void append4(const TopkShared& sh, const bool (&ok)[4
     }
     base += __popcll(m[e]);
   }
+}
+
+// Sampling plan of a long row's threshold: up to kSegs segments of kSegLen
+// consecutive candidates spread over the ncand candidates (nsamp samples),
+// and the rank among them whose key becomes the threshold: the expected rank
+// of the k-th best plus four standard deviations plus 8, so that with high
+// probability at least k candidates, and not many more, have a key at or
+// above it.  False when the row is too short for that.
+__device__ __forceinline__ bool sample_plan(int ncand, int k, int& seg_len, int& nsamp, int& rank) {
+  seg_len = ncand / kSegs < kSegLen ? ncand / kSegs : kSegLen;
+  nsamp = seg_len * kSegs;
+  const double expect = static_cast<double>(k) * nsamp / ncand;
+  rank = static_cast<int>(expect + 4.0 * sqrt(expect) + 8.0);
+  return nsamp >= 1024 && rank < nsamp;
+}
+
+// The threshold key from the samples' keys (thread tid holds samples tid +
+// j kLongThreads, keys of samples past nsamp are ignored): the radix levels
+// find the rank-th largest (sample index as tie-break) to 22 key bits (sign,
+// exponent and 13 mantissa bits, within about 1e-4 of that sample: enough);
+// the key prefix with its low bits zero is at most that sample's key.
+template <int KPT>
+__device__ __forceinline__ uint32_t sampled_threshold_t(const TopkShared& sh, const uint32_t (&skey)[KPT],
+                                                        int nsamp, int rank) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0;
+  int pbits = 0, need = rank;
+  while (true) {
+    int bsel, above, cntb;
+    auto each = [&](auto f) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int e = tid + j * kLongThreads;
+        if (e < nsamp) f(composite(skey[j], e));
+      }
+    };
+    radix_level(sh, pbits, prefix, need, each, bsel, above, cntb);
+    need -= above;
+    prefix = (prefix << kDigit) | static_cast<uint64_t>(bsel);
+    pbits += kDigit;
+    if (cntb == 1 || pbits >= 22) break;
+  }
+  return pbits >= 32 ? static_cast<uint32_t>(prefix >> (pbits - 32))
+                     : static_cast<uint32_t>(prefix << (32 - pbits));
+}
+__device__ __forceinline__ uint32_t sampled_threshold(const TopkShared& sh,
+                                                      const uint32_t (&skey)[kSampPerThread],
+                                                      int nsamp, int rank) {
+  return sampled_threshold_t<kSampPerThread>(sh, skey, nsamp, rank);
+}
+
+// The selection bitmap of a row (nwords words) as ascending column indices
+// into dst[0, max_out), padded with -1, and their number into *count.
+__device__ void emit_bitmap(const TopkShared& sh, int nwords, int32_t* dst, int max_out, int32_t* count) {
+  const int tid = threadIdx.x;
+  const int wpt = (nwords + kLongThreads - 1) / kLongThreads;
+  const int w0 = tid * wpt;
+  int mine = 0;
+  for (int w = w0; w < w0 + wpt && w < nwords; ++w) mine += __popc(sh.bitmap[w]);
+  int total;
+  int pos = block_excl_scan(mine, sh.tmp, total);
+  for (int w = w0; w < w0 + wpt && w < nwords; ++w) {
+    uint32_t bits = sh.bitmap[w];
+    while (bits) {
+      const int bpos = __ffs(bits) - 1;
+      bits &= bits - 1;
+      dst[pos++] = w * 32 + bpos;
+    }
+  }
+  for (int p = total + tid; p < max_out; p += kLongThreads) dst[p] = -1;
+  if (tid == 0) *count = total;
 }
 
 // One 512-thread work-group per row.
@@ -377,13 +441,10 @@ __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
     for (int i = fa + tid; i < fb; i += kLongThreads) atomicOr(&sh.bitmap[i >> 5], 1u << (i & 31));
   } else if (k > 0) {
     bool done = false;
-    const int seg_len = ncand / kSegs < kSegLen ? ncand / kSegs : kSegLen;
-    const int nsamp = seg_len * kSegs;
-    const double expect = static_cast<double>(k) * nsamp / ncand;
-    int rank = static_cast<int>(expect + 4.0 * sqrt(expect) + 8.0);
-    if (nsamp >= 1024 && rank < nsamp) {
-      // 1. the rank-th largest sample (sample index as tie-break); each thread
-      //    keeps its samples' keys in registers for the radix levels
+    int seg_len, nsamp, rank;
+    if (sample_plan(ncand, k, seg_len, nsamp, rank)) {
+      // 1. the rank-th largest sample; each thread keeps its samples' keys in
+      //    registers for the radix levels
       const int seg_stride = ncand / kSegs;
       // Sample e sits at fa + (e / seg_len) seg_stride + e % seg_len.  The
       // thread's samples are e = tid + j kLongThreads: segment and offset
@@ -407,40 +468,13 @@ __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
 #pragma unroll
       for (int j = 0; j < kSampPerThread; ++j)
         skey[j] = tid + j * kLongThreads < nsamp ? order_key(sval[j]) : 0u;
-      uint64_t prefix = 0;
-      int pbits = 0, need = rank;
-      while (true) {
-        int bsel, above, cntb;
-        auto each = [&](auto f) {
-#pragma unroll
-          for (int j = 0; j < kSampPerThread; ++j) {
-            const int e = tid + j * kLongThreads;
-            if (e < nsamp) f(composite(skey[j], e));
-          }
-        };
-        radix_level(sh, pbits, prefix, need, each, bsel, above, cntb);
-        need -= above;
-        prefix = (prefix << kDigit) | static_cast<uint64_t>(bsel);
-        pbits += kDigit;
-        // 22 key bits (sign, exponent and 13 mantissa bits) place the
-        // threshold within about 1e-4 of the sample at that rank: enough
-        if (cntb == 1 || pbits >= 22) break;
-      }
-      // the key prefix, low bits zero: at most the sample key at that rank
-      const uint32_t t_low = pbits >= 32 ? static_cast<uint32_t>(prefix >> (pbits - 32))
-                                          : static_cast<uint32_t>(prefix << (32 - pbits));
+      const uint32_t t_low = sampled_threshold(sh, skey, nsamp, rank);
       __syncthreads();
       if (tid == 0) *sh.nbuf = 0;
       __syncthreads();
-      // 2. collect every candidate with key >= t_low.  For a value that is not
-      //    NaN, key(v) >= t_low is v >= f_low, f_low the float whose key is
-      //    t_low; a t_low at or below the key of -inf takes every value (NaN
-      //    ranks as -inf), one above the key of +inf gives a NaN f_low that
-      //    no value passes.
-      const bool take_all = t_low <= 0x007fffffu;
-      const float f_low = (t_low & 0x80000000u) ? __uint_as_float(t_low & 0x7fffffffu)
-                                                : __uint_as_float(~t_low);
-      auto qualifies = [&](float v) { return take_all || v >= f_low; };
+      // 2. collect every candidate with key >= t_low (as a float test)
+      const KeyThreshold thr(t_low);
+      auto qualifies = [&](float v) { return thr.qualifies(v); };
       const bool aligned = ((reinterpret_cast<uintptr_t>(s) & 15) == 0);
       const int a0 = aligned ? ((fa + 3) & ~3) : fb;
       const int a1 = aligned ? (fb & ~3) : fb;
@@ -542,24 +576,15 @@ __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
   }
   __syncthreads();
 
-  // compact the bitmap into ascending column indices
-  const int wpt = (nwords + kLongThreads - 1) / kLongThreads;
-  const int w0 = tid * wpt;
-  int mine = 0;
-  for (int w = w0; w < w0 + wpt && w < nwords; ++w) mine += __popc(sh.bitmap[w]);
-  int total;
-  int pos = block_excl_scan(mine, sh.tmp, total);
-  int32_t* dst = idx_out + row * max_out;
-  for (int w = w0; w < w0 + wpt && w < nwords; ++w) {
-    uint32_t bits = sh.bitmap[w];
-    while (bits) {
-      const int bpos = __ffs(bits) - 1;
-      bits &= bits - 1;
-      dst[pos++] = w * 32 + bpos;
-    }
-  }
-  for (int p = total + tid; p < max_out; p += kLongThreads) dst[p] = -1;
-  if (tid == 0) count_out[row] = total;
+  emit_bitmap(sh, nwords, idx_out + row * max_out, max_out, count_out + row);
+}
+
+// Candidate buffer of a long row: k plus a quarter plus 1024 (the sampled
+// threshold overshoots k by a few standard deviations), at most kMaxCap.
+int topk_cap(int k) {
+  int cap = k + k / 4 + 1024;
+  cap = ((cap + 63) / 64) * 64;
+  return cap > kMaxCap ? kMaxCap : cap;
 }
 
 hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_t* valid_len,
@@ -577,11 +602,7 @@ hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_
     else SA_TOPK_W(16);
 #undef SA_TOPK_W
   } else {
-    // candidate buffer: k plus a quarter plus 1024 (the sampled threshold
-    // overshoots k by a few standard deviations), at most kMaxCap
-    int cap = k_const + k_const / 4 + 1024;
-    cap = ((cap + 63) / 64) * 64;
-    if (cap > kMaxCap) cap = kMaxCap;
+    const int cap = topk_cap(k_const);
     const size_t lds = topk_lds_bytes(cols, cap);
     // allow the largest size this kernel ever asks for (above the 64 KB default)
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_block_kernel),
@@ -591,6 +612,256 @@ hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_
     topk_block_kernel<<<dim3(static_cast<unsigned>(rows)), kLongThreads, lds, st>>>(
         scores, cols, valid_len, k_per_row, k_const, n_sink, n_local, idx_out, max_out, count_out, cap);
   }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fused token top-k
+// The decode step's token selection without a score array ("FASA:
+// Frequency-aware Sparse Attention", sec. 2.B items 1 and 2: token importance
+// from the dominant chunks, then the critical subset T_t).  Three kernels:
+//  1. token_thr_kernel, one work-group per (batch, KV head): a sampled
+//     threshold for each of the group's query heads, from the scores of
+//     kSegs x kSegLenF sampled tokens (each sample's slab row read once for
+//     all heads).  Rows with k = 0 or k >= their length get a threshold
+//     nothing passes, rows too short to sample one that takes every token.
+//  2. the token scoring kernel in collect mode (token_score.hip): the same
+//     scores as the scoring entry point; tokens at or above the threshold go
+//     to per-wave candidate lists (no atomics).
+//  3. token_select_kernel, one work-group per row: the exact top-k of the
+//     candidates gathered into LDS; when a list overflowed or their number is
+//     not in [k, cap] (an unlucky sample), the exact radix select over all
+//     tokens with their scores recomputed by the same arithmetic.  The
+//     threshold only steers how many candidates come back, so the result is
+//     the top-k of the scores whatever it is.
+// The slab row of a token is the 2 n_dom dominant channels (NDC), read as
+// 16-byte words.
+
+constexpr int kSegLenF = 64;                                  // samples a segment (at most)
+constexpr int kSampPerThreadF = kSegs * kSegLenF / kLongThreads;  // 8
+
+// A row's candidate buffer in the fused selection: twice k plus 1024 (a
+// threshold sampled from kSegs x kSegLenF tokens overshoots k by more), at
+// most kMaxCap.
+int token_topk_cap(int k) {
+  int cap = 2 * k + 1024;
+  cap = ((cap + 63) / 64) * 64;
+  return cap > kMaxCap ? kMaxCap : cap;
+}
+
+// The scaled dominant query slice of row `row` in slab channel order, as the
+// scoring kernel stages it: thread t < NDC writes channel t.
+template <typename T, int NDC>
+__device__ __forceinline__ void stage_query_slice(float* s_q, const T* __restrict__ q, int64_t row,
+                                                  int g, int d, const int32_t* __restrict__ dom,
+                                                  int n_dom, float scale) {
+  const int tid = threadIdx.x;
+  if (tid < NDC) {
+    float v = 0.f;
+    if (tid < 2 * n_dom) {
+      const int qc = (dom[g * n_dom + (tid % n_dom)] + (tid >= n_dom ? d / 2 : 0)) & (d - 1);
+      v = Elem<T>::load1(q + row * d + qc) * scale;
+    }
+    s_q[tid] = v;
+  }
+}
+
+__device__ __forceinline__ int clamp_len(int L, int Lmax) { return L < 0 ? 0 : (L > Lmax ? Lmax : L); }
+
+template <typename T, int NDC, int GRP>
+__global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
+    const T* __restrict__ q, const T* __restrict__ kdom, int Hq, int Hkv, int Lmax, int d,
+    const int32_t* __restrict__ cache_len, const int32_t* __restrict__ dom, int n_dom, float scale,
+    int k_top, uint32_t* __restrict__ thr) {
+  constexpr int R16 = NDC * static_cast<int>(sizeof(T)) / 16;  // 16-byte words a slab row
+  static_assert(R16 >= 1 && R16 <= 8, "slab rows of 16 to 128 bytes");
+  constexpr int KPT = kSampPerThreadF;
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ int s_tmp[kLongThreads / kWave + 4];
+  __shared__ __attribute__((aligned(16))) float s_q[GRP][NDC];
+  TopkShared sh{};
+  sh.hist = s_hist;
+  sh.tmp = s_tmp;
+  sh.pick = s_tmp + kLongThreads / kWave;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / Hkv;
+  const int g = blockIdx.x % Hkv;
+  const int64_t row0 = static_cast<int64_t>(b) * Hq + g * GRP;  // the group's first row
+  const int n = clamp_len(cache_len[b], Lmax);
+  const int k = k_top;
+  // uniform over the work-group: all threads return here or none
+  if (k <= 0 || k >= n) {
+    if (tid < GRP) thr[row0 + tid] = kNoCandidates;
+    return;
+  }
+  const int seg_len = n / kSegs < kSegLenF ? n / kSegs : kSegLenF;
+  const int nsamp = seg_len * kSegs;
+  const double expect = static_cast<double>(k) * nsamp / n;
+  const int rank = static_cast<int>(expect + 4.0 * sqrt(expect) + 8.0);
+  if (nsamp < 1024 || rank >= nsamp) {
+    if (tid < GRP) thr[row0 + tid] = 0u;  // take every token
+    return;
+  }
+#pragma unroll
+  for (int hh = 0; hh < GRP; ++hh)
+    stage_query_slice<T, NDC>(&s_q[hh][0], q, row0 + hh, g, d, dom, n_dom, scale);
+  __syncthreads();
+  const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * NDC;
+  // sample e = tid + j kLongThreads sits at (e / seg_len) seg_stride + e % seg_len
+  // (segment / offset stepped without a division); a sample past nsamp reads
+  // token 0 and its keys are dropped
+  const int seg_stride = n / kSegs;
+  const int seg_step = kLongThreads / seg_len, off_step = kLongThreads % seg_len;
+  int seg = tid / seg_len, off = tid % seg_len;
+  uint4 w[KPT][R16];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool in = tid + j * kLongThreads < nsamp;
+    const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(in ? seg * seg_stride + off : 0) * NDC);
+#pragma unroll
+    for (int c = 0; c < R16; ++c) w[j][c] = src[c];
+    seg += seg_step;
+    off += off_step;
+    if (off >= seg_len) { off -= seg_len; ++seg; }
+  }
+  uint32_t skey[GRP][KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    float kv[NDC];
+    load_slab_row<T, NDC>(reinterpret_cast<const T*>(&w[j][0]), kv);
+    const bool in = tid + j * kLongThreads < nsamp;
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh) skey[hh][j] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
+  }
+#pragma unroll
+  for (int hh = 0; hh < GRP; ++hh) {
+    const uint32_t t_low = sampled_threshold_t<KPT>(sh, skey[hh], nsamp, rank);
+    if (tid == 0) thr[row0 + hh] = t_low;
+  }
+}
+
+template <typename T, int NDC>
+__global__ __launch_bounds__(kLongThreads) void token_select_kernel(
+    const T* __restrict__ q, const T* __restrict__ kdom, int Hq, int Hkv, int Lmax, int d,
+    const int32_t* __restrict__ cache_len, const int32_t* __restrict__ dom, int n_dom, float scale,
+    int k_top, TokenCollect col, int cap, int32_t* __restrict__ idx_out, int max_out,
+    int32_t* __restrict__ count_out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t topk_lds[];
+  __shared__ __attribute__((aligned(16))) float s_q[NDC];
+  const TopkShared sh = topk_views(topk_lds, Lmax, cap);
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int b = static_cast<int>(row / Hq);
+  const int g = static_cast<int>(row % Hq) / (Hq / Hkv);
+  const int n = clamp_len(cache_len[b], Lmax);
+  const int k = k_top;
+  const int nwords = (n + 31) / 32;
+  for (int w = tid; w < nwords; w += kLongThreads) sh.bitmap[w] = 0u;
+  if (tid == 0) *sh.nbuf = 0;
+  __syncthreads();
+  if (k >= n) {
+    for (int i = tid; i < n; i += kLongThreads) atomicOr(&sh.bitmap[i >> 5], 1u << (i & 31));
+  } else if (k > 0) {
+    // gather the (tile, wave) lists: thread j < nsub owns list j
+    const int nsub = col.tiles * kCollectWaves;  // <= kLongThreads (Lmax <= 262144)
+    const int cj = tid < nsub ? col.cnt[row * nsub + tid] : 0;
+    const bool over = __syncthreads_or(cj > kCollectSlots);
+    int total;
+    const int at = block_excl_scan(cj, sh.tmp, total);
+    if (!over && total >= k && total <= cap) {
+      if (tid < nsub) {
+        const uint64_t* src = col.cand + (row * nsub + tid) * kCollectSlots;
+        for (int i = 0; i < cj; ++i) sh.cbuf[at + i] = src[i];
+      }
+      __syncthreads();
+      select_in_lds(sh, total, k);
+    } else {
+      // every token, its score recomputed exactly as the scoring kernel has it
+      stage_query_slice<T, NDC>(s_q, q, row, g, d, dom, n_dom, scale);
+      __syncthreads();
+      const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * NDC;
+      auto val = [&](int i) {
+        float kv[NDC];
+        load_slab_row<T, NDC>(kb + static_cast<int64_t>(i) * NDC, kv);
+        return token_dot<NDC>(s_q, kv);
+      };
+      select_from_source(sh, val, 0, n, k);
+    }
+  }
+  __syncthreads();
+  emit_bitmap(sh, nwords, idx_out + row * max_out, max_out, count_out + row);
+}
+
+// Workspace: thresholds [rows], list counts [rows, tiles, waves] and lists
+// [rows, tiles, waves, kCollectSlots], each part 256-byte aligned.
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+size_t token_topk_ws_bytes(int64_t rows, int Lmax) {
+  const size_t tiles = static_cast<size_t>((Lmax + kCollectTile - 1) / kCollectTile);
+  const size_t lists = static_cast<size_t>(rows) * tiles * kCollectWaves;
+  return align256(static_cast<size_t>(rows) * 4) + align256(lists * 4) + lists * kCollectSlots * 8;
+}
+
+hipError_t launch_token_topk(const void* q, const void* k_dom, int dtype, int B, int Hq, int Hkv,
+                             int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
+                             int n_dom, float scale, int k_top, int32_t* idx_out, int max_out,
+                             int32_t* count_out, void* ws, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(B) * Hq;
+  if (rows == 0) return hipSuccess;
+  const int cap = token_topk_cap(k_top);
+  const int tiles = (Lmax + kCollectTile - 1) / kCollectTile;
+  const size_t lists = static_cast<size_t>(rows) * tiles * kCollectWaves;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  uint32_t* thr = reinterpret_cast<uint32_t*>(w);
+  int* cnt = reinterpret_cast<int*>(w + align256(static_cast<size_t>(rows) * 4));
+  uint64_t* cand = reinterpret_cast<uint64_t*>(w + align256(static_cast<size_t>(rows) * 4) + align256(lists * 4));
+  const TokenCollect col{thr, cnt, cand, tiles};
+  const size_t lds = topk_lds_bytes(Lmax, cap);
+  const int ndc = 2 * n_dom;
+  const int grp = Hq / Hkv;
+#define SA_TT_G(T, C, G)                                                                            \
+  token_thr_kernel<T, C, G><<<dim3(static_cast<unsigned>(B * Hkv)), kLongThreads, 0, st>>>(        \
+      qq, kk, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, scale, k_top, thr)
+#define SA_TT(T, C)                                                                                 \
+  do {                                                                                              \
+    const auto* qq = static_cast<const T*>(q);                                                      \
+    const auto* kk = static_cast<const T*>(k_dom);                                                  \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&token_select_kernel<T, C>),   \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,                  \
+                                       static_cast<int>(topk_lds_bytes(kMaxLongCols, kMaxCap)));    \
+    if (e != hipSuccess) return e;                                                                  \
+    switch (grp) {                                                                                  \
+      case 1: SA_TT_G(T, C, 1); break;                                                              \
+      case 2: SA_TT_G(T, C, 2); break;                                                              \
+      case 4: SA_TT_G(T, C, 4); break;                                                              \
+      case 8: SA_TT_G(T, C, 8); break;                                                              \
+      default: return hipErrorInvalidValue;                                                         \
+    }                                                                                               \
+    e = hipGetLastError();                                                                          \
+    if (e != hipSuccess) return e;                                                                  \
+    e = launch_token_collect(q, k_dom, dtype, B, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, scale,    \
+                             col, st);                                                              \
+    if (e != hipSuccess) return e;                                                                  \
+    token_select_kernel<T, C><<<dim3(static_cast<unsigned>(rows)), kLongThreads, lds, st>>>(        \
+        qq, kk, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, scale, k_top, col, cap, idx_out, max_out,  \
+        count_out);                                                                                 \
+  } while (0)
+  if (dtype == kBF16) {
+    switch (ndc) {
+      case 8: SA_TT(uint16_t, 8); break;
+      case 16: SA_TT(uint16_t, 16); break;
+      case 32: SA_TT(uint16_t, 32); break;
+      case 64: SA_TT(uint16_t, 64); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (ndc) {
+      case 8: SA_TT(float, 8); break;
+      case 16: SA_TT(float, 16); break;
+      case 32: SA_TT(float, 32); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef SA_TT
+#undef SA_TT_G
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ Decode ("FASA: Frequency-aware Sparse Attention"):
     sa_rope_apply   -> the decode query rotated at position L_b - 1
     sa_token_score  -> dominant-chunk token scores
     sa_topk_select  -> top-k tokens
+      (dominant-slab layout: sa_token_topk does both without a score array)
     sa_sparse_attn_decode -> split-K attention over the selected tokens
 """
 from __future__ import annotations
@@ -22,9 +23,10 @@ import math
 import numpy as np
 import torch
 
-from . import (SA_OP_BLOCK_SCORE, SA_OP_DECODE, prefill_row_params, sa_block_score,
-               sa_kv_cache_append, sa_rope_apply, sa_sfa_sparsify, sa_sparse_attn_decode,
-               sa_sparse_attn_prefill, sa_token_score, sa_topk_select, workspace_bytes)
+from . import (SA_OP_BLOCK_SCORE, SA_OP_DECODE, SA_OP_TOKEN_TOPK, prefill_row_params,
+               sa_block_score, sa_kv_cache_append, sa_rope_apply, sa_sfa_sparsify,
+               sa_sparse_attn_decode, sa_sparse_attn_prefill, sa_token_score, sa_token_topk,
+               sa_topk_select, workspace_bytes)
 
 
 class PrefillLayer:
@@ -182,8 +184,12 @@ class DecodeCache:
 
 
 class DecodeStep:
+    """One decode step.  ``fused`` (default: the slab layout) scores and
+    selects the tokens with sa_token_topk, which writes no score array;
+    otherwise sa_token_score then sa_topk_select (the same selection)."""
+
     def __init__(self, q_raw, k, v, cache_len, dom_pairs, *, theta, top_k, slab=False, k_rest=None,
-                 sm_scale=None, cache_len_host=None):
+                 sm_scale=None, cache_len_host=None, fused=None):
         self.q_raw, self.k, self.v, self.k_rest = q_raw, k, v, k_rest
         B, Hq, d = q_raw.shape
         Hkv, L = v.shape[1], v.shape[2]
@@ -195,7 +201,15 @@ class DecodeStep:
         # position of the decoding token per batch row: cache_len - 1 (int32, [B])
         self.pos = (cache_len - 1).to(torch.int32).contiguous()
         self.q_rope = torch.empty_like(q_raw)
-        self.scores = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        self.fused = slab if fused is None else bool(fused)
+        if self.fused and not slab:
+            raise ValueError("the fused token top-k reads the dominant slab layout")
+        if self.fused:
+            self.scores = None
+            self.ws_sel = torch.empty(workspace_bytes(SA_OP_TOKEN_TOPK, rows=B * Hq, cols=L,
+                                                      max_k=top_k), dtype=torch.uint8, device=dev)
+        else:
+            self.scores = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
         self.valid_len = cache_len.repeat_interleave(Hq).to(torch.int32).contiguous()
         self.tok_idx = torch.empty((B, Hq, top_k), dtype=torch.int32, device=dev)
         self.tok_cnt = torch.empty((B, Hq), dtype=torch.int32, device=dev)
@@ -217,6 +231,10 @@ class DecodeStep:
         sa_topk_select(self.scores, self.tok_idx, self.tok_cnt, k_const=self.top_k,
                        valid_len=self.valid_len)
 
+    def score_select(self):
+        sa_token_topk(self.q_rope, self.k, self.cache_len, self.dom, self.tok_idx, self.tok_cnt,
+                      self.ws_sel, sm_scale=self.scale, k_top=self.top_k)
+
     def attend(self):
         sa_sparse_attn_decode(self.q_rope, self.k, self.v, self.tok_idx, self.tok_cnt, self.out,
                               self.ws, sm_scale=self.scale, cache_len=self.cache_len,
@@ -225,7 +243,10 @@ class DecodeStep:
 
     def run(self):
         self.rope()
-        self.score()
-        self.select()
+        if self.fused:
+            self.score_select()
+        else:
+            self.score()
+            self.select()
         self.attend()
         return self.out

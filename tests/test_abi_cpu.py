@@ -144,9 +144,40 @@ def test_validation_errors_before_launch():
     assert L.sa_sfa_sparsify(None, None, 1, 0, 128, 16, None) == sa.SA_OK
 
 
+def test_token_topk_validation():
+    """sa_token_topk: argument checks on the host, no launch."""
+    import long_context_sparse_apply_amd as sa
+    L = sa.lib
+    P = lambda: ctypes.c_void_p(16)  # noqa: E731 (never dereferenced: every call fails a check)
+    ws_ok = sa.workspace_bytes(sa.SA_OP_TOKEN_TOPK, rows=16, cols=4096, max_k=256)
+
+    def tt(q=True, dtype=1, B=2, Hq=8, Hkv=2, Lmax=4096, d=128, n_dom=16, k=256, max_out=256,
+           ws=True, wsb=None):
+        return L.sa_token_topk(P() if q else None, P(), dtype, B, Hq, Hkv, Lmax, d, P(), P(),
+                               n_dom, 0.1, k, P(), max_out, P(), P() if ws else None,
+                               ws_ok if wsb is None else wsb, None)
+    assert tt(q=False) == sa.SA_ERR_NULL
+    assert tt(dtype=7) == sa.SA_ERR_DTYPE
+    assert tt(Lmax=0) == sa.SA_ERR_SHAPE
+    assert tt(Lmax=300000) == sa.SA_ERR_SHAPE
+    assert tt(Hq=7) == sa.SA_ERR_SHAPE
+    assert tt(Hq=6, Hkv=2) == sa.SA_ERR_UNSUPPORTED
+    assert tt(n_dom=0) == sa.SA_ERR_RANGE
+    assert tt(k=-1) == sa.SA_ERR_RANGE
+    assert tt(max_out=255) == sa.SA_ERR_RANGE
+    assert tt(n_dom=48) == sa.SA_ERR_UNSUPPORTED          # 192-byte slab rows
+    assert tt(n_dom=2) == sa.SA_ERR_UNSUPPORTED           # 8-byte slab rows
+    assert tt(dtype=0, n_dom=32) == sa.SA_ERR_UNSUPPORTED  # fp32: 256-byte slab rows
+    assert tt(ws=False) == sa.SA_ERR_WORKSPACE
+    assert tt(wsb=ws_ok - 1) == sa.SA_ERR_WORKSPACE
+
+
 def test_workspace_sizes():
     import long_context_sparse_apply_amd as sa
     assert sa.workspace_bytes(sa.SA_OP_TOPK, 100, 1000) == 0
+    # thresholds and counts, then per row up to k + k/4 + 1024 (64-aligned) composites
+    assert sa.workspace_bytes(sa.SA_OP_TOKEN_TOPK, rows=2048, cols=131072, max_k=4096) >= 2048 * 6144 * 8
+    assert sa.workspace_bytes(sa.SA_OP_TOKEN_TOPK, rows=0, cols=10, max_k=4) == 0
     n = 1 * (32 + 8) * 256
     assert sa.workspace_bytes(sa.SA_OP_BLOCK_SCORE, n, 128) >= n * 128 * 4
     assert sa.workspace_bytes(99) == 0

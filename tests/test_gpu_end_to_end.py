@@ -136,7 +136,17 @@ def _compare_decode(cfg, step, x, batches, kv_heads, k_amb=None):
     scale = cfg.d ** -0.5
     P = cfg.d // 2
     g_q = _host(step.q_rope)
-    g_s = _host(step.scores)
+    if step.scores is None:
+        # the fused token top-k writes no scores: take them from the scoring
+        # entry point (the same arithmetic) to check its selection against
+        import long_context_sparse_apply_amd as sa
+        s = torch.empty((step.B, step.Hq, step.L), dtype=torch.float32, device=DEV)
+        sa.sa_token_score(step.q_rope, step.k, s, step.cache_len, step.dom, sm_scale=step.scale,
+                          slab=True, k_rest=step.k_rest)
+        torch.cuda.synchronize()
+        g_s = _host(s)
+    else:
+        g_s = _host(step.scores)
     g_idx, g_cnt = step.tok_idx.cpu().numpy(), step.tok_cnt.cpu().numpy()
     g_out = _host(step.out)
     q_rot = O.decode_query(x["q_raw"].astype(np.float64), x["lens"], cfg.theta)

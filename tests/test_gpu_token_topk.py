@@ -1,0 +1,127 @@
+"""GPU parity of the fused token top-k (sa_token_topk) against the two calls it
+replaces, sa_token_score then sa_topk_select: the selections must be equal
+bit for bit (indices and counts), on the same device inputs.
+
+The two-step path is itself checked against the fp64 oracle elsewhere (staged
+and end-to-end decode tests), so equality here carries that parity over.
+Cases cover the sampled-threshold path, rows too short to sample (every token
+a candidate), k at or above a row's length, empty rows, several slab widths,
+group sizes and both dtypes, and the exact fallback: a cache whose scores all
+tie sends every token past the threshold, so the candidate list overflows and
+the row is selected again from recomputed scores.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import workloads as W
+from tests.parity_utils import say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import long_context_sparse_apply_amd as m
+    import synth.device  # noqa: F401
+    return m
+
+
+def _two_step(sa, q_rope, k_dom, lens, dom, scale, k_top):
+    B, Hq, _ = q_rope.shape
+    Lmax = k_dom.shape[2]
+    scores = torch.empty((B, Hq, Lmax), dtype=torch.float32, device=DEV)
+    sa.sa_token_score(q_rope, k_dom, scores, lens, dom, sm_scale=scale, slab=True)
+    idx = torch.empty((B, Hq, k_top), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((B, Hq), dtype=torch.int32, device=DEV)
+    sa.sa_topk_select(scores, idx, cnt, k_const=k_top,
+                      valid_len=lens.repeat_interleave(Hq).to(torch.int32).contiguous())
+    return idx, cnt
+
+
+def _fused(sa, q_rope, k_dom, lens, dom, scale, k_top, max_out=None):
+    B, Hq, _ = q_rope.shape
+    Lmax = k_dom.shape[2]
+    max_out = k_top if max_out is None else max_out
+    ws = torch.empty(sa.workspace_bytes(sa.SA_OP_TOKEN_TOPK, rows=B * Hq, cols=Lmax, max_k=k_top),
+                     dtype=torch.uint8, device=DEV)
+    idx = torch.full((B, Hq, max_out), 12345, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, Hq), 12345, dtype=torch.int32, device=DEV)
+    sa.sa_token_topk(q_rope, k_dom, lens, dom, idx, cnt, ws, sm_scale=scale, k_top=k_top)
+    return idx, cnt
+
+
+def _inputs(dtype, B, Hq, Hkv, Lmax, n_dom, lens, seed, tie=False):
+    q = synth.gaussian_tensor(seed, synth.TID_Q, (B, Hq, 128), dtype)
+    kd = synth.gaussian_tensor(seed, synth.TID_K, (B, Hkv, Lmax, 2 * n_dom), dtype)
+    if tie:
+        kd[:] = kd[:, :, :1, :]  # every token the same key: every score ties
+    g = np.random.default_rng(seed)
+    dom = np.sort(np.stack([g.choice(64, n_dom, replace=False) for _ in range(Hkv)]), axis=1)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return (torch.from_numpy(q).to(DEV).to(tdt), torch.from_numpy(kd).to(DEV).to(tdt),
+            torch.tensor(lens, dtype=torch.int32, device=DEV),
+            torch.from_numpy(dom.astype(np.int32)).to(DEV).contiguous())
+
+
+CASES = [  # name, dtype, B, Hq, Hkv, Lmax, n_dom, lens, k_top, tie
+    ("bf16-32k-sampled", "bf16", 2, 8, 2, 32768, 16, [32768, 20000], 1024, False),
+    ("bf16-64k-grp8", "bf16", 1, 8, 1, 65536, 16, [65536], 2048, False),
+    ("bf16-ragged-short", "bf16", 4, 4, 4, 9000, 16, [9000, 700, 1, 0], 512, False),
+    ("bf16-k-above-len", "bf16", 2, 4, 2, 3000, 16, [3000, 2500], 2800, False),
+    ("bf16-narrow-slab", "bf16", 1, 4, 1, 20000, 4, [19999], 300, False),
+    ("bf16-wide-slab", "bf16", 1, 2, 1, 20000, 32, [20000], 640, False),
+    ("f32-sampled", "f32", 2, 4, 2, 20000, 8, [20000, 15000], 700, False),
+    ("f32-narrow", "f32", 1, 2, 2, 6000, 4, [6000], 100, False),
+    ("bf16-all-tied-fallback", "bf16", 1, 4, 1, 16384, 16, [16384], 512, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_token_topk_equals_score_then_select(sa, case):
+    name, dtype, B, Hq, Hkv, Lmax, n_dom, lens, k_top, tie = case
+    say(f"case: token top-k {name}")
+    q, kd, lens_t, dom = _inputs(dtype, B, Hq, Hkv, Lmax, n_dom, lens, 40 + len(name), tie)
+    scale = 128 ** -0.5
+    ri, rc = _two_step(sa, q, kd, lens_t, dom, scale, k_top)
+    fi, fc = _fused(sa, q, kd, lens_t, dom, scale, k_top)
+    torch.cuda.synchronize()
+    assert torch.equal(fc, rc), (fc.cpu(), rc.cpu())
+    assert torch.equal(fi, ri)
+    # counts are min(k, length): a row never loses a selected token
+    exp = np.minimum(k_top, np.repeat(np.asarray(lens), Hq)).reshape(B, Hq)
+    assert np.array_equal(fc.cpu().numpy(), exp)
+
+
+def test_token_topk_pads_wider_output(sa):
+    """max_out above k_top: the selection is the same and the rest is -1."""
+    q, kd, lens_t, dom = _inputs("bf16", 1, 4, 1, 12000, 16, [11000], 77)
+    scale = 128 ** -0.5
+    ri, rc = _two_step(sa, q, kd, lens_t, dom, scale, 256)
+    fi, fc = _fused(sa, q, kd, lens_t, dom, scale, 256, max_out=300)
+    torch.cuda.synchronize()
+    assert torch.equal(fc, rc)
+    assert torch.equal(fi[..., :256], ri)
+    assert bool((fi[..., 256:] == -1).all())
+
+
+def test_token_topk_decode_c5_shape(sa):
+    """The 128K slab decode workload (batch 64, top-4096), as the bench runs
+    it: the fused step's selection equals the two-step selection."""
+    from long_context_sparse_apply_amd.pipeline import DecodeStep
+    import synth.device as SD
+    cfg = W.C5
+    dt = SD.decode_tensors(cfg)
+    fused = DecodeStep(dt["q_raw"], dt["k"], dt["v"], dt["lens"], dt["dom"], theta=cfg.theta,
+                       top_k=cfg.k, slab=True, k_rest=dt["k_rest"], fused=True)
+    fused.rope()
+    fused.score_select()
+    ri, rc = _two_step(sa, fused.q_rope, fused.k, fused.cache_len, fused.dom, fused.scale, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.tok_cnt, rc)
+    assert torch.equal(fused.tok_idx, ri)
