@@ -36,6 +36,14 @@ template <> struct TokElem<float> {
   }
 };
 
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt not waited on): the LDS stores
+// before a barrier complete too, which the barrier does not wait for.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
 // ROW: channels per stored row (d, or 2*n_dom for the slab); NDC: dominant
 // channels per head (2*n_dom) rounded up; GRP: query heads per KV head.
 template <typename T, int ROW, int GRP, int NDC>
@@ -55,9 +63,9 @@ struct TokenScoreShape {
 
 // COLLECT: instead of storing the scores, append each token whose score
 // passes its row's threshold key (and lies below cache_len) to the wave's own
-// candidate list of that row and tile (blockIdx.x); the wave counts in
-// registers and writes its counts at the end (entries past the slots are
-// dropped, the count stays true).
+// candidate list of that row and tile (blockIdx.x), as (score bits << 32 |
+// token); the wave counts in scalars and writes its counts at the end
+// (entries past the slots are dropped, the count stays true).
 template <typename T, int ROW, int GRP, int NDC, bool SLAB, bool COLLECT>
 __global__ __launch_bounds__(256) void token_score_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int Hq, int Hkv, int Lmax, int d,
@@ -69,13 +77,13 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   static_assert(!SLAB || ROW == NDC, "the slab row is exactly the dominant channels");
   __shared__ __attribute__((aligned(1024))) uint8_t sk0[CHB];
   __shared__ __attribute__((aligned(1024))) uint8_t sk1[CHB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk2[COLLECT ? CHB : 16];  // collect: 3rd stage
   __shared__ __attribute__((aligned(16))) float s_q[GRP][NDC];
   __shared__ int s_off[NDC];
-  __shared__ uint32_t s_thr[GRP];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wid = tid / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int P = d / 2;
@@ -86,22 +94,29 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   nch = nch < chunks_per_wg ? nch : chunks_per_wg;
   const uint8_t* kb = reinterpret_cast<const uint8_t*>(k + (static_cast<int64_t>(b) * Hkv + g) * Lmax * ROW);
 
-  // stage chunk c's rows (rows past the cache end re-read its last row)
+  // stage chunk c's rows (rows past the cache end re-read its last row); the
+  // collect instances load through a buffer resource over this (b, KV head)'s
+  // rows (at most 64 MiB), whose LDS writes the compiler tracks per buffer
+  const auto rsrc = buffer_rsrc(kb, Lmax * ROWB);
+  auto issue_one = [&](int t0, int last, int j, uint8_t* buf) {
+    const int ins = wid * LPW + j;
+    const int off = ins * 1024 + lane * 16;
+    const int row = off / ROWB;
+    const int pos = (off % ROWB) >> 4;
+    const int src_row = row < last ? row : last;
+    const int byte = (t0 + src_row) * ROWB + ((pos ^ (row % CPR)) << 4);
+    if constexpr (COLLECT)
+      lds_dma16_buf(rsrc, byte, buf + ins * 1024);
+    else
+      lds_dma16(kb + byte, buf + ins * 1024);
+  };
   auto issue = [&](int c, uint8_t* buf) {
     const int t0 = tb + c * CT;
     const int last = Lmax - 1 - t0;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int ins = wid * LPW + j;
-      const int off = ins * 1024 + lane * 16;
-      const int row = off / ROWB;
-      const int pos = (off % ROWB) >> 4;
-      const int src_row = row < last ? row : last;
-      lds_dma16(kb + static_cast<int64_t>(t0 + src_row) * ROWB + ((pos ^ (row % CPR)) << 4),
-                buf + ins * 1024);
-    }
+    for (int j = 0; j < LPW; ++j) issue_one(t0, last, j, buf);
   };
-  if (nch > 0) issue(0, sk0);
+  if (!COLLECT && nch > 0) issue(0, sk0);
 
   // query slices (dominant channels, pre-scaled) and the stored channel of each
   for (int e = tid; e < GRP * NDC; e += 256) {
@@ -114,7 +129,6 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     }
     s_q[hh][j] = v;
   }
-  if (COLLECT && tid < GRP) s_thr[tid] = col.thr[static_cast<int64_t>(b) * Hq + g * GRP + tid];
   if (tid < NDC) {
     int c = 0;
     if (tid < ndc) c = SLAB ? tid : (dom[g * n_dom + (tid % n_dom)] + (tid >= n_dom ? P : 0)) & (d - 1);
@@ -123,14 +137,43 @@ __global__ __launch_bounds__(256) void token_score_kernel(
 
   static_assert(!COLLECT || (CT == 256 && Sh::HGS0 == 1),
                 "collect mode: every thread scores all heads of its token, one 64-token share a wave");
-  int wcnt[HPT];  // collect mode: this wave's candidates a head so far (equal over the wave)
+  // collect mode, per head (uniform over the wave): candidates so far, the
+  // threshold as a float test, and the wave's list
+  int wcnt[HPT];
+  float f_low[HPT];
+  bool take_all[HPT];
+  uint64_t* lst[HPT];
 #pragma unroll
-  for (int u = 0; u < HPT; ++u) wcnt[u] = 0;
+  for (int u = 0; u < HPT; ++u) {
+    wcnt[u] = 0;
+    if constexpr (COLLECT) {
+      const int64_t srow = static_cast<int64_t>(b) * Hq + g * GRP + u;
+      const KeyThreshold kt(col.thr[srow]);
+      f_low[u] = kt.f_low;
+      take_all[u] = kt.take_all;
+      lst[u] = col.cand + ((srow * col.tiles + blockIdx.x) * kCollectWaves + wid) * kCollectSlots;
+    }
+  }
   const int r = tid % CT;              // this thread's token within a chunk
   const int hg = tid / CT;             // its head group (HGS groups of HPT heads)
-  const bool active = hg * HPT < GRP;
+  // (collect mode: one head group of all GRP heads, every thread scores)
+  const bool active = COLLECT || hg * HPT < GRP;
   const int rx = r % CPR;
 
+  // collect mode: a chunk's candidates wait in registers (pend_*) and are
+  // stored at the start of the next step, before its loads
+  uint64_t pend_v[COLLECT ? HPT : 1];
+  int pend_s[COLLECT ? HPT : 1];
+  bool pend_p[COLLECT ? HPT : 1];
+#pragma unroll
+  for (int u = 0; u < (COLLECT ? HPT : 1); ++u) pend_p[u] = false;
+  auto flush = [&]() {
+    if constexpr (COLLECT) {
+#pragma unroll
+      for (int u = 0; u < HPT; ++u)
+        if (pend_p[u]) lst[u][static_cast<uint32_t>(pend_s[u])] = pend_v[u];
+    }
+  };
   auto score_chunk = [&](int c, const uint8_t* buf) {
     if (!active) return;
     const int t = tb + c * CT + r;
@@ -157,20 +200,23 @@ __global__ __launch_bounds__(256) void token_score_kernel(
         kv[j] = TokElem<T>::lds(rowp + ((((byte >> 4) ^ rx)) << 4) + (byte & 15));
       }
     }
+    // (t < Lmax too: the selection's row length is cache_len clamped to Lmax)
+    const bool tin = t < L && t < Lmax;
 #pragma unroll
     for (int u = 0; u < HPT; ++u) {
       const int hh = hg * HPT + u;
       const float acc = token_dot<NDC>(&s_q[hh][0], kv);
       const int64_t srow = static_cast<int64_t>(b) * Hq + g * GRP + hh;
       if constexpr (COLLECT) {
-        // (t < Lmax too: the selection's row length is cache_len clamped to Lmax)
-        const bool ok = t < L && t < Lmax && KeyThreshold(s_thr[hh]).qualifies(acc);
+        // (KeyThreshold::qualifies with the test's parts held per head)
+        const bool ok = tin & (take_all[u] | (acc >= f_low[u]));
         const uint64_t m = __ballot(ok);
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-        const int pos = wcnt[u] + __popcll(m & below);
-        if (ok && pos < kCollectSlots)
-          col.cand[((srow * col.tiles + blockIdx.x) * kCollectWaves + wid) * kCollectSlots + pos] =
-              composite(order_key(acc), t);
+        const int pos = wcnt[u] + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                      static_cast<uint32_t>(m >> 32),
+                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+        pend_p[u] = ok & (pos < kCollectSlots);
+        pend_s[u] = pos;
+        pend_v[u] = (static_cast<uint64_t>(__float_as_uint(acc)) << 32) | static_cast<uint32_t>(t);
         wcnt[u] += __popcll(m);
       } else {
         if (t < Lmax) scores[srow * Lmax + t] = (t < L) ? acc : -INFINITY;
@@ -178,18 +224,48 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     }
   };
 
-  // wait for chunk c, barrier (every share landed; every thread is done with
-  // chunk c - 1, whose buffer is free), issue chunk c + 1, score chunk c
-  for (int c = 0; c < nch; c += 2) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (c + 1 < nch) issue(c + 1, sk1);
-    score_chunk(c, sk0);
-    if (c + 1 >= nch) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (c + 2 < nch) issue(c + 2, sk0);
-    score_chunk(c + 1, sk1);
+  if constexpr (COLLECT) {
+    // Three stages, two chunks in flight.  Step c: wait for chunk c's loads,
+    // barrier (every share landed; chunk c - 1's buffer is free), store
+    // chunk c - 1's candidates, issue chunk c + 2 into the free buffer, score
+    // chunk c.  A wave's vector memory operations complete in issue order,
+    // and after chunk c's loads it issued only chunk c - 2's stores and
+    // chunk c + 1's loads (LPW, if any): waiting until LPW remain covers
+    // chunk c (and those stores, one step after they were issued).
+    if (nch > 0) issue(0, sk0);
+    if (nch > 1) issue(1, sk1);
+    auto step = [&](int c, const uint8_t* cur, uint8_t* ahead) {
+      if (c + 1 < nch)
+        wait_vm_lgkm0<LPW>();
+      else
+        wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+      flush();
+      if (c + 2 < nch) issue(c + 2, ahead);
+      score_chunk(c, cur);
+    };
+    for (int c = 0; c < nch; c += 3) {
+      step(c, sk0, sk2);
+      if (c + 1 >= nch) break;
+      step(c + 1, sk1, sk0);
+      if (c + 2 >= nch) break;
+      step(c + 2, sk2, sk1);
+    }
+    flush();
+  } else {
+    // wait for chunk c, barrier (every share landed; every thread is done
+    // with chunk c - 1, whose buffer is free), issue chunk c + 1, score c
+    for (int c = 0; c < nch; c += 2) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (c + 1 < nch) issue(c + 1, sk1);
+      score_chunk(c, sk0);
+      if (c + 1 >= nch) break;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (c + 2 < nch) issue(c + 2, sk0);
+      score_chunk(c + 1, sk1);
+    }
   }
 
   // collect mode: the wave's counts of this tile, one a head

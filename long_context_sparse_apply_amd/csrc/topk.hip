@@ -228,11 +228,13 @@ __device__ __forceinline__ void radix_level(const TopkShared& sh, int pbits, uin
 }
 
 // Exact selection of the `need` largest composites among cbuf[0, nbuf): marks
-// their columns in the bitmap.
-__device__ void select_in_lds(const TopkShared& sh, int nbuf, int need) {
+// their columns in the bitmap.  Where every composite is known to share its
+// top pbits0 bits (prefix0), the first level starts below them.
+__device__ void select_in_lds(const TopkShared& sh, int nbuf, int need, uint64_t prefix0 = 0,
+                              int pbits0 = 0) {
   const int tid = threadIdx.x;
-  uint64_t prefix = 0;
-  int pbits = 0;
+  uint64_t prefix = prefix0;
+  int pbits = pbits0;
   while (true) {
     int bsel, above, cntb;
     auto each = [&](auto f) {
@@ -747,6 +749,10 @@ __global__ __launch_bounds__(kLongThreads) void token_select_kernel(
     int32_t* __restrict__ count_out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t topk_lds[];
   __shared__ __attribute__((aligned(16))) float s_q[NDC];
+  constexpr int kMaxLists = kMaxLongCols / kCollectTile * kCollectWaves;
+  static_assert(kMaxLists <= kLongThreads, "a thread a list in the count scan");
+  __shared__ int s_at[kMaxLists], s_cn[kMaxLists];  // each list's place and length
+  __shared__ uint64_t s_lo[kLongThreads / kWave], s_hi[kLongThreads / kWave];
   const TopkShared sh = topk_views(topk_lds, Lmax, cap);
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -768,12 +774,59 @@ __global__ __launch_bounds__(kLongThreads) void token_select_kernel(
     int total;
     const int at = block_excl_scan(cj, sh.tmp, total);
     if (!over && total >= k && total <= cap) {
+      // Four threads a list, each taking every fourth entry; a round issues
+      // all its loads before any store (a list past 64 entries takes more
+      // rounds; a round's reads stay in the list's kCollectSlots slots).  The
+      // smallest and largest composite come along for the select.
       if (tid < nsub) {
-        const uint64_t* src = col.cand + (row * nsub + tid) * kCollectSlots;
-        for (int i = 0; i < cj; ++i) sh.cbuf[at + i] = src[i];
+        s_at[tid] = at;
+        s_cn[tid] = cj;
       }
       __syncthreads();
-      select_in_lds(sh, total, k);
+      uint64_t lo = ~0ull, hi = 0ull;
+      for (int j = tid >> 2; j < nsub; j += kLongThreads / 4) {
+        const int nj = s_cn[j], aj = s_at[j];
+        const uint64_t* src = col.cand + (row * nsub + j) * kCollectSlots + (tid & 3);
+        for (int base = 0; base < nj; base += 64) {
+          uint64_t v[16];
+#pragma unroll
+          for (int m = 0; m < 16; ++m) v[m] = src[base + 4 * m];
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            const int i = base + (tid & 3) + 4 * m;
+            if (i < nj) {
+              // (score bits, token) -> the composite the selection compares
+              const uint64_t c = composite(order_key(__uint_as_float(static_cast<uint32_t>(v[m] >> 32))),
+                                           static_cast<int>(static_cast<uint32_t>(v[m])));
+              sh.cbuf[aj + i] = c;
+              lo = c < lo ? c : lo;
+              hi = c > hi ? c : hi;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        const uint64_t a = __shfl_xor(lo, o, kWave), c = __shfl_xor(hi, o, kWave);
+        lo = a < lo ? a : lo;
+        hi = c > hi ? c : hi;
+      }
+      if ((tid & (kWave - 1)) == 0) {
+        s_lo[tid / kWave] = lo;
+        s_hi[tid / kWave] = hi;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < kLongThreads / kWave; ++w) {
+        lo = s_lo[w] < lo ? s_lo[w] : lo;
+        hi = s_hi[w] > hi ? s_hi[w] : hi;
+      }
+      // every candidate lies in [lo, hi], so all share the bits above the
+      // highest bit where lo and hi differ (composites are unique: lo < hi
+      // unless there is one candidate)
+      int pb = __clzll(static_cast<long long>(lo ^ hi));
+      pb = pb > 63 ? 63 : pb;
+      select_in_lds(sh, total, k, pb > 0 ? hi >> (64 - pb) : 0ull, pb);
     } else {
       // every token, its score recomputed exactly as the scoring kernel has it
       stage_query_slice<T, NDC>(s_q, q, row, g, d, dom, n_dom, scale);

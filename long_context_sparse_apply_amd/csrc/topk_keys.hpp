@@ -49,7 +49,7 @@ constexpr uint32_t kNoCandidates = 0xffffffffu;
 // row (b * Hq + h), so no list is shared and no atomic is needed: per (row,
 // tile, wave) the number of qualifying tokens (it may exceed the slots: the
 // selection then reads the row again) and the first kCollectSlots of them as
-// (key, token) composites.
+// score bits << 32 | token (the selection forms the composites).
 constexpr int kCollectTile = 4096;
 constexpr int kCollectWaves = 4;
 constexpr int kCollectSlots = 256;
