@@ -376,7 +376,7 @@ def run_decode(cfg, steps, warmup, torch, flush):
         t["score_hbm_frac"] = key_bytes / (t["score_select_us"] * 1e-6) / PEAK_HBM_BPS
         # the two calls it replaces, on the same inputs, for comparison
         two = DecodeStep(dt["q_raw"], dt["k"], dt["v"], dt["lens"], dt["dom"], theta=cfg.theta,
-                         top_k=cfg.k, slab=True, k_rest=dt["k_rest"], fused=False)
+                         top_k=cfg.k, slab=bool(cfg.slab), k_rest=dt["k_rest"], fused=False)
         two.rope()
 
         def score_then_select():

@@ -173,15 +173,16 @@ sa_status sa_token_score(const void* q_rope, const void* k, const void* k_rest, 
 
 /*
  * sa_token_topk -- FASA Token Importance Predictor and the critical token
- * subset in one call (sec. 2.B items 1 and 2), for the dominant-slab cache
- * layout (sec. 2.C), without writing the score array.
- *   The result equals, bit for bit, sa_token_score(q_rope, k_dom, NULL, dtype,
- *   B, Hq, Hkv, Lmax, d, cache_len, dom_pairs, n_dom, slab = 1, sm_scale,
+ * subset in one call (sec. 2.B items 1 and 2), without writing the score
+ * array; standard or dominant-slab cache layout (sec. 2.C).
+ *   The result equals, bit for bit, sa_token_score(q_rope, k, NULL, dtype,
+ *   B, Hq, Hkv, Lmax, d, cache_len, dom_pairs, n_dom, slab, sm_scale,
  *   scores) followed by sa_topk_select(scores, B*Hq, Lmax, valid_len = row
  *   b*Hq + h -> cache_len[b], k_per_row = NULL, k_const = k_top, n_sink = 0,
  *   n_local = 0, idx_out, max_out, count_out).
- *   q_rope [B, Hq, d]; k_dom [B, Hkv, Lmax, 2*n_dom] (the slab); cache_len,
- *   dom_pairs as in sa_token_score.  2*n_dom channels of dtype must take 16,
+ *   q_rope [B, Hq, d]; k: the standard cache [B, Hkv, Lmax, d] (slab = 0) or
+ *   the slab [B, Hkv, Lmax, 2*n_dom] (slab = 1); cache_len, dom_pairs as in
+ *   sa_token_score.  With the slab, 2*n_dom channels of dtype must take 16,
  *   32, 64 or 128 bytes (SA_ERR_UNSUPPORTED otherwise).
  *   idx_out [B*Hq, max_out] int32 (max_out >= k_top), count_out [B*Hq].
  *   ws: sa_workspace_bytes(SA_OP_TOKEN_TOPK, B*Hq, Lmax, 0, 0, 0) bytes: per
@@ -197,11 +198,10 @@ sa_status sa_token_score(const void* q_rope, const void* k, const void* k_rest, 
  *         SA_ERR_RANGE (n_dom, k_top < 0, max_out < k_top), SA_ERR_WORKSPACE,
  *         SA_ERR_UNSUPPORTED (Hq / Hkv not 1, 2, 4, 8; slab width), SA_ERR_DTYPE.
  */
-sa_status sa_token_topk(const void* q_rope, const void* k_dom, sa_dtype dtype, int B, int Hq,
-                        int Hkv, int Lmax, int d, const int32_t* cache_len,
-                        const int32_t* dom_pairs, int n_dom, float sm_scale, int k_top,
-                        int32_t* idx_out, int max_out, int32_t* count_out, void* ws,
-                        size_t ws_bytes, void* stream);
+sa_status sa_token_topk(const void* q_rope, const void* k, sa_dtype dtype, int B, int Hq, int Hkv,
+                        int Lmax, int d, const int32_t* cache_len, const int32_t* dom_pairs,
+                        int n_dom, int slab, float sm_scale, int k_top, int32_t* idx_out,
+                        int max_out, int32_t* count_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sa_topk_select -- per-row selection (Prism sec. 1: keep a subset of

@@ -47,7 +47,7 @@ def _load() -> ctypes.CDLL:
         "sa_kv_cache_append": [P, P, I, I, I, I, I, I, P, D, I, P, I, P, P, P, P],
         "sa_block_score": [P, P, I, I, I, I, I, I, D, I, I, I, F, I, P, F, P, P, P, P, P, SZ, P],
         "sa_token_score": [P, P, P, I, I, I, I, I, I, P, P, I, I, F, P, P],
-        "sa_token_topk": [P, P, I, I, I, I, I, I, P, P, I, F, I, P, I, P, P, SZ, P],
+        "sa_token_topk": [P, P, I, I, I, I, I, I, P, P, I, I, F, I, P, I, P, P, SZ, P],
         "sa_topk_select": [P, I64, I, P, P, I, I, I, P, I, P, P, SZ, P],
         "sa_sparse_attn_prefill": [P, P, P, I, I, I, I, I, I, I, P, P, I, I, F, P, P, P],
         "sa_sparse_attn_decode": [P, P, P, P, I, I, I, I, I, I, P, P, I, I, P, P, I, F, P, P, P,
@@ -225,15 +225,16 @@ def sa_token_score(q_rope, k, scores, cache_len, dom_pairs, *, sm_scale: float, 
     return scores
 
 
-def sa_token_topk(q_rope, k_dom, cache_len, dom_pairs, idx_out, count_out, ws, *, sm_scale: float,
-                  k_top: int, stream=None):
-    """Token scores from the dominant slab and their top-k per (b, h) row in one
-    call, without a score array: q_rope [B,Hq,d], k_dom [B,Hkv,Lmax,2*n_dom] ->
+def sa_token_topk(q_rope, k, cache_len, dom_pairs, idx_out, count_out, ws, *, sm_scale: float,
+                  k_top: int, slab: bool = True, stream=None):
+    """Token scores from the dominant channels and their top-k per (b, h) row
+    in one call, without a score array: q_rope [B,Hq,d], k the slab
+    [B,Hkv,Lmax,2*n_dom] (slab=True) or the standard cache [B,Hkv,Lmax,d] ->
     idx_out [B,Hq,max_out] (max_out >= k_top), count_out [B,Hq].  ws: uint8 of
     workspace_bytes(SA_OP_TOKEN_TOPK, rows=B*Hq, cols=Lmax, max_k=k_top)."""
     torch = _torch()
     _check(q_rope, "q_rope", ndim=3)
-    _check(k_dom, "k_dom", q_rope.dtype, 4)
+    _check(k, "k", q_rope.dtype, 4)
     _check(cache_len, "cache_len", torch.int32, 1)
     _check(dom_pairs, "dom_pairs", torch.int32, 2)
     _check(idx_out, "idx_out", torch.int32)
@@ -242,14 +243,15 @@ def sa_token_topk(q_rope, k_dom, cache_len, dom_pairs, idx_out, count_out, ws, *
         raise ValueError("sa_token_topk needs its workspace")
     _check(ws, "ws")
     B, Hq, dd = q_rope.shape
-    Hkv, Lmax = k_dom.shape[1], k_dom.shape[2]
+    Hkv, Lmax = k.shape[1], k.shape[2]
     n_dom = dom_pairs.shape[1]
     max_out = idx_out.shape[-1]
     if idx_out.numel() != B * Hq * max_out or count_out.numel() != B * Hq:
         raise ValueError("idx_out / count_out do not match the (b, h) rows")
-    _call("sa_token_topk", _ptr(q_rope), _ptr(k_dom), _dtype_code(q_rope), B, Hq, Hkv, Lmax, dd,
-          _ptr(cache_len), _ptr(dom_pairs), n_dom, float(sm_scale), int(k_top), _ptr(idx_out),
-          max_out, _ptr(count_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _call("sa_token_topk", _ptr(q_rope), _ptr(k), _dtype_code(q_rope), B, Hq, Hkv, Lmax, dd,
+          _ptr(cache_len), _ptr(dom_pairs), n_dom, 1 if slab else 0, float(sm_scale), int(k_top),
+          _ptr(idx_out), max_out, _ptr(count_out), _ptr(ws), ws.numel() * ws.element_size(),
+          _stream(stream))
     return idx_out, count_out
 
 

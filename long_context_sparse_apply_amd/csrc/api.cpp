@@ -137,28 +137,30 @@ sa_status sa_token_score(const void* q_rope, const void* k, const void* k_rest, 
                                          as_stream(stream)));
 }
 
-sa_status sa_token_topk(const void* q_rope, const void* k_dom, sa_dtype dtype, int B, int Hq,
+sa_status sa_token_topk(const void* q_rope, const void* k, sa_dtype dtype, int B, int Hq,
                         int Hkv, int Lmax, int d, const int32_t* cache_len,
-                        const int32_t* dom_pairs, int n_dom, float sm_scale, int k_top,
+                        const int32_t* dom_pairs, int n_dom, int slab, float sm_scale, int k_top,
                         int32_t* idx_out, int max_out, int32_t* count_out, void* ws,
                         size_t ws_bytes, void* stream) {
   if (!dtype_ok(dtype)) return SA_ERR_DTYPE;
-  if (!q_rope || !k_dom || !cache_len || !dom_pairs || !idx_out || !count_out) return SA_ERR_NULL;
+  if (!q_rope || !k || !cache_len || !dom_pairs || !idx_out || !count_out) return SA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Lmax < 1 || Lmax > 262144 ||
       !head_dim_ok(d))
     return SA_ERR_SHAPE;
   const int grp = Hq / Hkv;
   if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return SA_ERR_UNSUPPORTED;
   if (n_dom < 1 || n_dom > d / 2 || k_top < 0 || max_out < 1 || max_out < k_top) return SA_ERR_RANGE;
-  // slab rows of 16 to 128 bytes in a power of two
-  const int row_bytes = 2 * n_dom * (dtype == SA_BF16 ? 2 : 4);
-  if (row_bytes < 16 || row_bytes > 128 || (row_bytes & (row_bytes - 1)) != 0)
-    return SA_ERR_UNSUPPORTED;
+  if (slab) {
+    // slab rows of 16 to 128 bytes in a power of two
+    const int row_bytes = 2 * n_dom * (dtype == SA_BF16 ? 2 : 4);
+    if (row_bytes < 16 || row_bytes > 128 || (row_bytes & (row_bytes - 1)) != 0)
+      return SA_ERR_UNSUPPORTED;
+  }
   const int64_t rows = static_cast<int64_t>(B) * Hq;
   if (!ws || ws_bytes < sa::token_topk_ws_bytes(rows, Lmax)) return SA_ERR_WORKSPACE;
-  return launched(sa::launch_token_topk(q_rope, k_dom, dtype, B, Hq, Hkv, Lmax, d, cache_len,
-                                        dom_pairs, n_dom, sm_scale, k_top, idx_out, max_out,
-                                        count_out, ws, as_stream(stream)));
+  return launched(sa::launch_token_topk(q_rope, k, dtype, B, Hq, Hkv, Lmax, d, cache_len,
+                                        dom_pairs, n_dom, slab ? 1 : 0, sm_scale, k_top, idx_out,
+                                        max_out, count_out, ws, as_stream(stream)));
 }
 
 sa_status sa_topk_select(const float* scores, int64_t rows, int cols, const int32_t* valid_len,

@@ -53,17 +53,18 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int dtype
 struct TokenCollect;
 
 // the scoring kernel in collect mode: tokens at or above their row's threshold
-// key appended to the row's candidate list (dominant-slab layout only)
-hipError_t launch_token_collect(const void* q, const void* k_dom, int dtype, int B, int Hq, int Hkv,
+// key appended to the row's candidate lists (standard or dominant-slab layout)
+hipError_t launch_token_collect(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
                                 int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
-                                int n_dom, float scale, const TokenCollect& col, hipStream_t st);
+                                int n_dom, int slab, float scale, const TokenCollect& col,
+                                hipStream_t st);
 
 // token scores and their top-k in one call, without a score array
 size_t token_topk_ws_bytes(int64_t rows, int Lmax);
-hipError_t launch_token_topk(const void* q, const void* k_dom, int dtype, int B, int Hq, int Hkv,
+hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
                              int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
-                             int n_dom, float scale, int k_top, int32_t* idx_out, int max_out,
-                             int32_t* count_out, void* ws, hipStream_t st);
+                             int n_dom, int slab, float scale, int k_top, int32_t* idx_out,
+                             int max_out, int32_t* count_out, void* ws, hipStream_t st);
 
 hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
                               int Lmax, int d, const int32_t* cache_len, const int32_t* dom,

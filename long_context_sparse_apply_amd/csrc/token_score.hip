@@ -77,7 +77,9 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   static_assert(!SLAB || ROW == NDC, "the slab row is exactly the dominant channels");
   __shared__ __attribute__((aligned(1024))) uint8_t sk0[CHB];
   __shared__ __attribute__((aligned(1024))) uint8_t sk1[CHB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sk2[COLLECT ? CHB : 16];  // collect: 3rd stage
+  // collect mode with chunks of at most 16 KB: a third stage
+  constexpr bool THREE = COLLECT && CHB <= 16384;
+  __shared__ __attribute__((aligned(1024))) uint8_t sk2[THREE ? CHB : 16];
   __shared__ __attribute__((aligned(16))) float s_q[GRP][NDC];
   __shared__ int s_off[NDC];
 
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
 #pragma unroll
     for (int j = 0; j < LPW; ++j) issue_one(t0, last, j, buf);
   };
-  if (!COLLECT && nch > 0) issue(0, sk0);
+  if (!THREE && nch > 0) issue(0, sk0);
 
   // query slices (dominant channels, pre-scaled) and the stored channel of each
   for (int e = tid; e < GRP * NDC; e += 256) {
@@ -135,10 +137,14 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     s_off[tid] = c * ES;  // byte offset of the channel within an unswizzled row
   }
 
-  static_assert(!COLLECT || (CT == 256 && Sh::HGS0 == 1),
-                "collect mode: every thread scores all heads of its token, one 64-token share a wave");
-  // collect mode, per head (uniform over the wave): candidates so far, the
-  // threshold as a float test, and the wave's list
+  static_assert(CT * Sh::HGS0 == 256, "a chunk's tokens times the head groups fill the work-group");
+  const int r = tid % CT;              // this thread's token within a chunk
+  const int hg = tid / CT;             // its head group (HGS groups of HPT heads)
+  // (one head group: every thread scores; known to the compiler in collect mode)
+  const bool active = (COLLECT && Sh::HGS0 == 1) || hg * HPT < GRP;
+  const int hh0 = active ? hg * HPT : 0;  // the group's first head (a valid one when idle)
+  // collect mode, per head of the thread's group (uniform over the wave):
+  // candidates so far, the threshold as a float test, and the wave's list
   int wcnt[HPT];
   float f_low[HPT];
   bool take_all[HPT];
@@ -147,17 +153,13 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   for (int u = 0; u < HPT; ++u) {
     wcnt[u] = 0;
     if constexpr (COLLECT) {
-      const int64_t srow = static_cast<int64_t>(b) * Hq + g * GRP + u;
+      const int64_t srow = static_cast<int64_t>(b) * Hq + g * GRP + (hh0 + u < GRP ? hh0 + u : 0);
       const KeyThreshold kt(col.thr[srow]);
       f_low[u] = kt.f_low;
       take_all[u] = kt.take_all;
       lst[u] = col.cand + ((srow * col.tiles + blockIdx.x) * kCollectWaves + wid) * kCollectSlots;
     }
   }
-  const int r = tid % CT;              // this thread's token within a chunk
-  const int hg = tid / CT;             // its head group (HGS groups of HPT heads)
-  // (collect mode: one head group of all GRP heads, every thread scores)
-  const bool active = COLLECT || hg * HPT < GRP;
   const int rx = r % CPR;
 
   // collect mode: a chunk's candidates wait in registers (pend_*) and are
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     }
   };
 
-  if constexpr (COLLECT) {
+  if constexpr (THREE) {
     // Three stages, two chunks in flight.  Step c: wait for chunk c's loads,
     // barrier (every share landed; chunk c - 1's buffer is free), store
     // chunk c - 1's candidates, issue chunk c + 2 into the free buffer, score
@@ -255,32 +257,40 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   } else {
     // wait for chunk c, barrier (every share landed; every thread is done
     // with chunk c - 1, whose buffer is free), issue chunk c + 1, score c
+    // (collect mode: each chunk's candidates are stored at once)
     for (int c = 0; c < nch; c += 2) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (c + 1 < nch) issue(c + 1, sk1);
       score_chunk(c, sk0);
+      flush();
       if (c + 1 >= nch) break;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (c + 2 < nch) issue(c + 2, sk0);
       score_chunk(c + 1, sk1);
+      flush();
     }
   }
 
-  // collect mode: the wave's counts of this tile, one a head
+  // collect mode: the wave's counts of this tile for every head of the
+  // group (zero for the heads of other waves' groups, whose lists it leaves)
   if constexpr (COLLECT) {
-    if (active && lane == 0) {
+    if (lane == 0) {
 #pragma unroll
-      for (int u = 0; u < HPT; ++u)
-        col.cnt[((static_cast<int64_t>(b) * Hq + g * GRP + hg * HPT + u) * col.tiles + blockIdx.x) *
-                    kCollectWaves + wid] = wcnt[u];
+      for (int hh = 0; hh < GRP; ++hh) {
+        int v = 0;
+#pragma unroll
+        for (int u = 0; u < HPT; ++u)
+          if (active && hg * HPT + u == hh) v = wcnt[u];
+        col.cnt[((static_cast<int64_t>(b) * Hq + g * GRP + hh) * col.tiles + blockIdx.x) * kCollectWaves + wid] = v;
+      }
     }
   }
 }
 
 // Scoring (COLLECT false: every score into `scores`) or candidate collection
-// for the fused token top-k (COLLECT true, slab layout only).
+// for the fused token top-k (COLLECT true).
 template <bool COLLECT>
 static hipError_t launch_scoring(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
                                  int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
@@ -302,15 +312,10 @@ static hipError_t launch_scoring(const void* q, const void* k, int dtype, int B,
     cpw /= 2;
   if (COLLECT && cpw * ct != kCollectTile) return hipErrorInvalidValue;
   const dim3 grid((per_head_chunks + cpw - 1) / cpw, Hkv, B);
-// (collect mode exists for slab rows of at most 128 bytes)
-#define SA_TS(T, R, G, C, SL)                                                                    \
-  if constexpr (!COLLECT || R * sizeof(T) <= 128) {                                              \
-    token_score_kernel<T, R, G, C, SL, COLLECT><<<grid, 256, 0, st>>>(                            \
-        static_cast<const T*>(q), static_cast<const T*>(k), Hq, Hkv, Lmax, d, cache_len, dom,     \
-        n_dom, scale, scores, cpw, col);                                                         \
-  } else {                                                                                       \
-    return hipErrorInvalidValue;                                                                 \
-  }
+#define SA_TS(T, R, G, C, SL)                                                                  \
+  token_score_kernel<T, R, G, C, SL, COLLECT><<<grid, 256, 0, st>>>(                            \
+      static_cast<const T*>(q), static_cast<const T*>(k), Hq, Hkv, Lmax, d, cache_len, dom,     \
+      n_dom, scale, scores, cpw, col)
 #define SA_TS_G(T, R, C, SL)                  \
   switch (grp) {                              \
     case 1: SA_TS(T, R, 1, C, SL); break;     \
@@ -337,8 +342,6 @@ static hipError_t launch_scoring(const void* q, const void* k, int dtype, int B,
       case 128: SA_TS_G(T, 128, 128, true) break;                      \
       default: return hipErrorInvalidValue;                            \
     }                                                                  \
-  } else if constexpr (COLLECT) {                                      \
-    return hipErrorInvalidValue;                                       \
   } else if (d == 128) {                                               \
     SA_TS_STD(T, 128)                                                  \
   } else {                                                             \
@@ -364,10 +367,11 @@ hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, in
                                scores, TokenCollect{}, st);
 }
 
-hipError_t launch_token_collect(const void* q, const void* k_dom, int dtype, int B, int Hq, int Hkv,
+hipError_t launch_token_collect(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
                                 int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
-                                int n_dom, float scale, const TokenCollect& col, hipStream_t st) {
-  return launch_scoring<true>(q, k_dom, dtype, B, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, 1, scale,
+                                int n_dom, int slab, float scale, const TokenCollect& col,
+                                hipStream_t st) {
+  return launch_scoring<true>(q, k, dtype, B, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, slab, scale,
                               nullptr, col, st);
 }
 

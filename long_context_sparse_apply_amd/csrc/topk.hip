@@ -669,15 +669,35 @@ __device__ __forceinline__ void stage_query_slice(float* s_q, const T* __restric
 
 __device__ __forceinline__ int clamp_len(int L, int Lmax) { return L < 0 ? 0 : (L > Lmax ? Lmax : L); }
 
-template <typename T, int NDC, int GRP>
+// Standard layout: the row channel of scored slot j, as the scoring kernel
+// reads it (slots past 2 n_dom read channel 0; their query value is 0).
+// Thread t < NDC writes slot t.
+template <int NDC>
+__device__ __forceinline__ void stage_channels(int* s_ch, int g, int d, const int32_t* __restrict__ dom,
+                                               int n_dom) {
+  const int tid = threadIdx.x;
+  if (tid < NDC)
+    s_ch[tid] = tid < 2 * n_dom ? (dom[g * n_dom + (tid % n_dom)] + (tid >= n_dom ? d / 2 : 0)) & (d - 1) : 0;
+}
+
+// One token's NDC scored channels from a standard row (all loads issued
+// before any use).
+template <typename T, int NDC>
+__device__ __forceinline__ void load_std_row(const T* __restrict__ row, const int* s_ch, float (&kv)[NDC]) {
+#pragma unroll
+  for (int j = 0; j < NDC; ++j) kv[j] = Elem<T>::load1(row + s_ch[j]);
+}
+
+template <typename T, int NDC, int GRP, bool SLAB>
 __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
     const T* __restrict__ q, const T* __restrict__ kdom, int Hq, int Hkv, int Lmax, int d,
     const int32_t* __restrict__ cache_len, const int32_t* __restrict__ dom, int n_dom, float scale,
     int k_top, uint32_t* __restrict__ thr) {
   constexpr int R16 = NDC * static_cast<int>(sizeof(T)) / 16;  // 16-byte words a slab row
-  static_assert(R16 >= 1 && R16 <= 8, "slab rows of 16 to 128 bytes");
+  static_assert(!SLAB || (R16 >= 1 && R16 <= 8), "slab rows of 16 to 128 bytes");
   constexpr int KPT = kSampPerThreadF;
   __shared__ uint32_t s_hist[kBins];
+  __shared__ int s_ch[NDC];
   __shared__ int s_tmp[kLongThreads / kWave + 4];
   __shared__ __attribute__((aligned(16))) float s_q[GRP][NDC];
   TopkShared sh{};
@@ -706,33 +726,62 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
 #pragma unroll
   for (int hh = 0; hh < GRP; ++hh)
     stage_query_slice<T, NDC>(&s_q[hh][0], q, row0 + hh, g, d, dom, n_dom, scale);
+  if (!SLAB) stage_channels<NDC>(s_ch, g, d, dom, n_dom);
   __syncthreads();
-  const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * NDC;
+  const int rowlen = SLAB ? NDC : d;
+  const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * rowlen;
   // sample e = tid + j kLongThreads sits at (e / seg_len) seg_stride + e % seg_len
   // (segment / offset stepped without a division); a sample past nsamp reads
   // token 0 and its keys are dropped
   const int seg_stride = n / kSegs;
   const int seg_step = kLongThreads / seg_len, off_step = kLongThreads % seg_len;
   int seg = tid / seg_len, off = tid % seg_len;
-  uint4 w[KPT][R16];
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const bool in = tid + j * kLongThreads < nsamp;
-    const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(in ? seg * seg_stride + off : 0) * NDC);
-#pragma unroll
-    for (int c = 0; c < R16; ++c) w[j][c] = src[c];
-    seg += seg_step;
-    off += off_step;
-    if (off >= seg_len) { off -= seg_len; ++seg; }
-  }
   uint32_t skey[GRP][KPT];
+  if constexpr (SLAB) {
+    uint4 w[KPT][R16];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    float kv[NDC];
-    load_slab_row<T, NDC>(reinterpret_cast<const T*>(&w[j][0]), kv);
-    const bool in = tid + j * kLongThreads < nsamp;
+    for (int j = 0; j < KPT; ++j) {
+      const bool in = tid + j * kLongThreads < nsamp;
+      const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(in ? seg * seg_stride + off : 0) * NDC);
 #pragma unroll
-    for (int hh = 0; hh < GRP; ++hh) skey[hh][j] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
+      for (int c = 0; c < R16; ++c) w[j][c] = src[c];
+      seg += seg_step;
+      off += off_step;
+      if (off >= seg_len) { off -= seg_len; ++seg; }
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      float kv[NDC];
+      load_slab_row<T, NDC>(reinterpret_cast<const T*>(&w[j][0]), kv);
+      const bool in = tid + j * kLongThreads < nsamp;
+#pragma unroll
+      for (int hh = 0; hh < GRP; ++hh) skey[hh][j] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
+    }
+  } else {
+    // standard rows: the scored channels of RND samples at a time
+    int tok[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      tok[j] = tid + j * kLongThreads < nsamp ? seg * seg_stride + off : 0;
+      seg += seg_step;
+      off += off_step;
+      if (off >= seg_len) { off -= seg_len; ++seg; }
+    }
+    constexpr int RND = NDC >= 64 ? 1 : (64 / NDC < KPT ? 64 / NDC : KPT);
+#pragma unroll
+    for (int j0 = 0; j0 < KPT; j0 += RND) {
+      float kv[RND][NDC];
+#pragma unroll
+      for (int jj = 0; jj < RND; ++jj)
+        load_std_row<T, NDC>(kb + static_cast<int64_t>(tok[j0 + jj]) * d, s_ch, kv[jj]);
+#pragma unroll
+      for (int jj = 0; jj < RND; ++jj) {
+        const bool in = tid + (j0 + jj) * kLongThreads < nsamp;
+#pragma unroll
+        for (int hh = 0; hh < GRP; ++hh)
+          skey[hh][j0 + jj] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv[jj])) : 0u;
+      }
+    }
   }
 #pragma unroll
   for (int hh = 0; hh < GRP; ++hh) {
@@ -741,7 +790,7 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
   }
 }
 
-template <typename T, int NDC>
+template <typename T, int NDC, bool SLAB>
 __global__ __launch_bounds__(kLongThreads) void token_select_kernel(
     const T* __restrict__ q, const T* __restrict__ kdom, int Hq, int Hkv, int Lmax, int d,
     const int32_t* __restrict__ cache_len, const int32_t* __restrict__ dom, int n_dom, float scale,
@@ -749,6 +798,7 @@ __global__ __launch_bounds__(kLongThreads) void token_select_kernel(
     int32_t* __restrict__ count_out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t topk_lds[];
   __shared__ __attribute__((aligned(16))) float s_q[NDC];
+  __shared__ int s_ch[NDC];
   constexpr int kMaxLists = kMaxLongCols / kCollectTile * kCollectWaves;
   static_assert(kMaxLists <= kLongThreads, "a thread a list in the count scan");
   __shared__ int s_at[kMaxLists], s_cn[kMaxLists];  // each list's place and length
@@ -830,11 +880,16 @@ __global__ __launch_bounds__(kLongThreads) void token_select_kernel(
     } else {
       // every token, its score recomputed exactly as the scoring kernel has it
       stage_query_slice<T, NDC>(s_q, q, row, g, d, dom, n_dom, scale);
+      if (!SLAB) stage_channels<NDC>(s_ch, g, d, dom, n_dom);
       __syncthreads();
-      const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * NDC;
+      const int rowlen = SLAB ? NDC : d;
+      const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * rowlen;
       auto val = [&](int i) {
         float kv[NDC];
-        load_slab_row<T, NDC>(kb + static_cast<int64_t>(i) * NDC, kv);
+        if constexpr (SLAB)
+          load_slab_row<T, NDC>(kb + static_cast<int64_t>(i) * NDC, kv);
+        else
+          load_std_row<T, NDC>(kb + static_cast<int64_t>(i) * d, s_ch, kv);
         return token_dot<NDC>(s_q, kv);
       };
       select_from_source(sh, val, 0, n, k);
@@ -853,10 +908,10 @@ size_t token_topk_ws_bytes(int64_t rows, int Lmax) {
   return align256(static_cast<size_t>(rows) * 4) + align256(lists * 4) + lists * kCollectSlots * 8;
 }
 
-hipError_t launch_token_topk(const void* q, const void* k_dom, int dtype, int B, int Hq, int Hkv,
+hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
                              int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
-                             int n_dom, float scale, int k_top, int32_t* idx_out, int max_out,
-                             int32_t* count_out, void* ws, hipStream_t st) {
+                             int n_dom, int slab, float scale, int k_top, int32_t* idx_out,
+                             int max_out, int32_t* count_out, void* ws, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(B) * Hq;
   if (rows == 0) return hipSuccess;
   const int cap = token_topk_cap(k_top);
@@ -868,49 +923,72 @@ hipError_t launch_token_topk(const void* q, const void* k_dom, int dtype, int B,
   uint64_t* cand = reinterpret_cast<uint64_t*>(w + align256(static_cast<size_t>(rows) * 4) + align256(lists * 4));
   const TokenCollect col{thr, cnt, cand, tiles};
   const size_t lds = topk_lds_bytes(Lmax, cap);
-  const int ndc = 2 * n_dom;
+  // scored slots: exactly 2 n_dom in the slab, a power of two of at least 8
+  // covering them in the standard layout (as the scoring kernel has it)
+  const int need = 2 * n_dom;
+  const int ndc = slab ? need : (need <= 8 ? 8 : need <= 16 ? 16 : need <= 32 ? 32 : need <= 64 ? 64 : 128);
   const int grp = Hq / Hkv;
-#define SA_TT_G(T, C, G)                                                                            \
-  token_thr_kernel<T, C, G><<<dim3(static_cast<unsigned>(B * Hkv)), kLongThreads, 0, st>>>(        \
+#define SA_TT_G(T, C, SL, G)                                                                        \
+  token_thr_kernel<T, C, G, SL><<<dim3(static_cast<unsigned>(B * Hkv)), kLongThreads, 0, st>>>(    \
       qq, kk, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, scale, k_top, thr)
-#define SA_TT(T, C)                                                                                 \
+#define SA_TT(T, C, SL)                                                                             \
   do {                                                                                              \
     const auto* qq = static_cast<const T*>(q);                                                      \
-    const auto* kk = static_cast<const T*>(k_dom);                                                  \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&token_select_kernel<T, C>),   \
+    const auto* kk = static_cast<const T*>(k);                                                      \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&token_select_kernel<T, C, SL>), \
                                        hipFuncAttributeMaxDynamicSharedMemorySize,                  \
                                        static_cast<int>(topk_lds_bytes(kMaxLongCols, kMaxCap)));    \
     if (e != hipSuccess) return e;                                                                  \
     switch (grp) {                                                                                  \
-      case 1: SA_TT_G(T, C, 1); break;                                                              \
-      case 2: SA_TT_G(T, C, 2); break;                                                              \
-      case 4: SA_TT_G(T, C, 4); break;                                                              \
-      case 8: SA_TT_G(T, C, 8); break;                                                              \
+      case 1: SA_TT_G(T, C, SL, 1); break;                                                          \
+      case 2: SA_TT_G(T, C, SL, 2); break;                                                          \
+      case 4: SA_TT_G(T, C, SL, 4); break;                                                          \
+      case 8: SA_TT_G(T, C, SL, 8); break;                                                          \
       default: return hipErrorInvalidValue;                                                         \
     }                                                                                               \
     e = hipGetLastError();                                                                          \
     if (e != hipSuccess) return e;                                                                  \
-    e = launch_token_collect(q, k_dom, dtype, B, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, scale,    \
+    e = launch_token_collect(q, k, dtype, B, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, slab, scale,  \
                              col, st);                                                              \
     if (e != hipSuccess) return e;                                                                  \
-    token_select_kernel<T, C><<<dim3(static_cast<unsigned>(rows)), kLongThreads, lds, st>>>(        \
+    token_select_kernel<T, C, SL><<<dim3(static_cast<unsigned>(rows)), kLongThreads, lds, st>>>(    \
         qq, kk, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, scale, k_top, col, cap, idx_out, max_out,  \
         count_out);                                                                                 \
   } while (0)
   if (dtype == kBF16) {
-    switch (ndc) {
-      case 8: SA_TT(uint16_t, 8); break;
-      case 16: SA_TT(uint16_t, 16); break;
-      case 32: SA_TT(uint16_t, 32); break;
-      case 64: SA_TT(uint16_t, 64); break;
-      default: return hipErrorInvalidValue;
+    if (slab) {
+      switch (ndc) {
+        case 8: SA_TT(uint16_t, 8, true); break;
+        case 16: SA_TT(uint16_t, 16, true); break;
+        case 32: SA_TT(uint16_t, 32, true); break;
+        case 64: SA_TT(uint16_t, 64, true); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (ndc) {
+        case 8: SA_TT(uint16_t, 8, false); break;
+        case 16: SA_TT(uint16_t, 16, false); break;
+        case 32: SA_TT(uint16_t, 32, false); break;
+        case 64: SA_TT(uint16_t, 64, false); break;
+        default: SA_TT(uint16_t, 128, false); break;
+      }
     }
   } else {
-    switch (ndc) {
-      case 8: SA_TT(float, 8); break;
-      case 16: SA_TT(float, 16); break;
-      case 32: SA_TT(float, 32); break;
-      default: return hipErrorInvalidValue;
+    if (slab) {
+      switch (ndc) {
+        case 8: SA_TT(float, 8, true); break;
+        case 16: SA_TT(float, 16, true); break;
+        case 32: SA_TT(float, 32, true); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (ndc) {
+        case 8: SA_TT(float, 8, false); break;
+        case 16: SA_TT(float, 16, false); break;
+        case 32: SA_TT(float, 32, false); break;
+        case 64: SA_TT(float, 64, false); break;
+        default: SA_TT(float, 128, false); break;
+      }
     }
   }
 #undef SA_TT

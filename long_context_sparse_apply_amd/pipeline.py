@@ -201,9 +201,10 @@ class DecodeStep:
         # position of the decoding token per batch row: cache_len - 1 (int32, [B])
         self.pos = (cache_len - 1).to(torch.int32).contiguous()
         self.q_rope = torch.empty_like(q_raw)
+        # (fused by default with the slab; with the standard layout the
+        # sampled threshold's scattered channel reads cost more than the score
+        # array it saves at the 64K shape, so two calls stay the default there)
         self.fused = slab if fused is None else bool(fused)
-        if self.fused and not slab:
-            raise ValueError("the fused token top-k reads the dominant slab layout")
         if self.fused:
             self.scores = None
             self.ws_sel = torch.empty(workspace_bytes(SA_OP_TOKEN_TOPK, rows=B * Hq, cols=L,
@@ -233,7 +234,7 @@ class DecodeStep:
 
     def score_select(self):
         sa_token_topk(self.q_rope, self.k, self.cache_len, self.dom, self.tok_idx, self.tok_cnt,
-                      self.ws_sel, sm_scale=self.scale, k_top=self.top_k)
+                      self.ws_sel, sm_scale=self.scale, k_top=self.top_k, slab=self.slab)
 
     def attend(self):
         sa_sparse_attn_decode(self.q_rope, self.k, self.v, self.tok_idx, self.tok_cnt, self.out,

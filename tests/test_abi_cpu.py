@@ -151,10 +151,10 @@ def test_token_topk_validation():
     P = lambda: ctypes.c_void_p(16)  # noqa: E731 (never dereferenced: every call fails a check)
     ws_ok = sa.workspace_bytes(sa.SA_OP_TOKEN_TOPK, rows=16, cols=4096, max_k=256)
 
-    def tt(q=True, dtype=1, B=2, Hq=8, Hkv=2, Lmax=4096, d=128, n_dom=16, k=256, max_out=256,
-           ws=True, wsb=None):
+    def tt(q=True, dtype=1, B=2, Hq=8, Hkv=2, Lmax=4096, d=128, n_dom=16, slab=1, k=256,
+           max_out=256, ws=True, wsb=None):
         return L.sa_token_topk(P() if q else None, P(), dtype, B, Hq, Hkv, Lmax, d, P(), P(),
-                               n_dom, 0.1, k, P(), max_out, P(), P() if ws else None,
+                               n_dom, slab, 0.1, k, P(), max_out, P(), P() if ws else None,
                                ws_ok if wsb is None else wsb, None)
     assert tt(q=False) == sa.SA_ERR_NULL
     assert tt(dtype=7) == sa.SA_ERR_DTYPE
@@ -168,6 +168,11 @@ def test_token_topk_validation():
     assert tt(n_dom=48) == sa.SA_ERR_UNSUPPORTED          # 192-byte slab rows
     assert tt(n_dom=2) == sa.SA_ERR_UNSUPPORTED           # 8-byte slab rows
     assert tt(dtype=0, n_dom=32) == sa.SA_ERR_UNSUPPORTED  # fp32: 256-byte slab rows
+    # the standard layout reads any n_dom of the full rows: no slab-width rule
+    assert tt(slab=0, n_dom=48, ws=False) == sa.SA_ERR_WORKSPACE
+    assert tt(slab=0, n_dom=2, ws=False) == sa.SA_ERR_WORKSPACE
+    assert tt(slab=0, d=96) == sa.SA_ERR_SHAPE
+    assert tt(slab=0, n_dom=65) == sa.SA_ERR_RANGE
     assert tt(ws=False) == sa.SA_ERR_WORKSPACE
     assert tt(wsb=ws_ok - 1) == sa.SA_ERR_WORKSPACE
 

@@ -142,7 +142,7 @@ def _compare_decode(cfg, step, x, batches, kv_heads, k_amb=None):
         import long_context_sparse_apply_amd as sa
         s = torch.empty((step.B, step.Hq, step.L), dtype=torch.float32, device=DEV)
         sa.sa_token_score(step.q_rope, step.k, s, step.cache_len, step.dom, sm_scale=step.scale,
-                          slab=True, k_rest=step.k_rest)
+                          slab=step.slab, k_rest=step.k_rest)
         torch.cuda.synchronize()
         g_s = _host(s)
     else:

@@ -1,6 +1,7 @@
 """GPU parity of the fused token top-k (sa_token_topk) against the two calls it
 replaces, sa_token_score then sa_topk_select: the selections must be equal
-bit for bit (indices and counts), on the same device inputs.
+bit for bit (indices and counts), on the same device inputs, for the
+dominant-slab and the standard cache layouts.
 
 The two-step path is itself checked against the fp64 oracle elsewhere (staged
 and end-to-end decode tests), so equality here carries that parity over.
@@ -32,11 +33,11 @@ def sa():
     return m
 
 
-def _two_step(sa, q_rope, k_dom, lens, dom, scale, k_top):
+def _two_step(sa, q_rope, k_dom, lens, dom, scale, k_top, slab=True):
     B, Hq, _ = q_rope.shape
     Lmax = k_dom.shape[2]
     scores = torch.empty((B, Hq, Lmax), dtype=torch.float32, device=DEV)
-    sa.sa_token_score(q_rope, k_dom, scores, lens, dom, sm_scale=scale, slab=True)
+    sa.sa_token_score(q_rope, k_dom, scores, lens, dom, sm_scale=scale, slab=slab)
     idx = torch.empty((B, Hq, k_top), dtype=torch.int32, device=DEV)
     cnt = torch.empty((B, Hq), dtype=torch.int32, device=DEV)
     sa.sa_topk_select(scores, idx, cnt, k_const=k_top,
@@ -44,7 +45,7 @@ def _two_step(sa, q_rope, k_dom, lens, dom, scale, k_top):
     return idx, cnt
 
 
-def _fused(sa, q_rope, k_dom, lens, dom, scale, k_top, max_out=None):
+def _fused(sa, q_rope, k_dom, lens, dom, scale, k_top, max_out=None, slab=True):
     B, Hq, _ = q_rope.shape
     Lmax = k_dom.shape[2]
     max_out = k_top if max_out is None else max_out
@@ -52,17 +53,17 @@ def _fused(sa, q_rope, k_dom, lens, dom, scale, k_top, max_out=None):
                      dtype=torch.uint8, device=DEV)
     idx = torch.full((B, Hq, max_out), 12345, dtype=torch.int32, device=DEV)
     cnt = torch.full((B, Hq), 12345, dtype=torch.int32, device=DEV)
-    sa.sa_token_topk(q_rope, k_dom, lens, dom, idx, cnt, ws, sm_scale=scale, k_top=k_top)
+    sa.sa_token_topk(q_rope, k_dom, lens, dom, idx, cnt, ws, sm_scale=scale, k_top=k_top, slab=slab)
     return idx, cnt
 
 
-def _inputs(dtype, B, Hq, Hkv, Lmax, n_dom, lens, seed, tie=False):
-    q = synth.gaussian_tensor(seed, synth.TID_Q, (B, Hq, 128), dtype)
-    kd = synth.gaussian_tensor(seed, synth.TID_K, (B, Hkv, Lmax, 2 * n_dom), dtype)
+def _inputs(dtype, B, Hq, Hkv, Lmax, n_dom, lens, seed, tie=False, slab=True, d=128):
+    q = synth.gaussian_tensor(seed, synth.TID_Q, (B, Hq, d), dtype)
+    kd = synth.gaussian_tensor(seed, synth.TID_K, (B, Hkv, Lmax, 2 * n_dom if slab else d), dtype)
     if tie:
         kd[:] = kd[:, :, :1, :]  # every token the same key: every score ties
     g = np.random.default_rng(seed)
-    dom = np.sort(np.stack([g.choice(64, n_dom, replace=False) for _ in range(Hkv)]), axis=1)
+    dom = np.sort(np.stack([g.choice(d // 2, n_dom, replace=False) for _ in range(Hkv)]), axis=1)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     return (torch.from_numpy(q).to(DEV).to(tdt), torch.from_numpy(kd).to(DEV).to(tdt),
             torch.tensor(lens, dtype=torch.int32, device=DEV),
@@ -98,6 +99,36 @@ def test_token_topk_equals_score_then_select(sa, case):
     assert np.array_equal(fc.cpu().numpy(), exp)
 
 
+STD_CASES = [  # name, dtype, d, B, Hq, Hkv, Lmax, n_dom, lens, k_top, tie
+    ("std-bf16-64k-c4-shape", "bf16", 128, 2, 8, 2, 65536, 16, [65536, 40000], 2048, False),
+    ("std-bf16-ragged", "bf16", 128, 4, 4, 4, 9000, 16, [9000, 700, 1, 0], 512, False),
+    ("std-bf16-grp1-n5", "bf16", 128, 1, 2, 2, 20000, 5, [19999], 300, False),
+    ("std-bf16-grp8-n40", "bf16", 128, 1, 8, 1, 30000, 40, [30000], 1000, False),
+    ("std-bf16-d64", "bf16", 64, 2, 4, 1, 16384, 8, [16384, 9000], 600, False),
+    ("std-f32", "f32", 128, 2, 4, 2, 20000, 16, [20000, 15000], 700, False),
+    ("std-bf16-k-above-len", "bf16", 128, 2, 4, 2, 3000, 16, [3000, 2500], 2800, False),
+    ("std-bf16-all-tied-fallback", "bf16", 128, 1, 4, 1, 16384, 16, [16384], 512, True),
+]
+
+
+@pytest.mark.parametrize("case", STD_CASES, ids=[c[0] for c in STD_CASES])
+def test_token_topk_standard_layout(sa, case):
+    """The standard cache layout (full rows, the dominant channels read from
+    each): the fused selection equals score-then-select bit for bit."""
+    name, dtype, d, B, Hq, Hkv, Lmax, n_dom, lens, k_top, tie = case
+    say(f"case: token top-k {name}")
+    q, kd, lens_t, dom = _inputs(dtype, B, Hq, Hkv, Lmax, n_dom, lens, 90 + len(name), tie,
+                                 slab=False, d=d)
+    scale = d ** -0.5
+    ri, rc = _two_step(sa, q, kd, lens_t, dom, scale, k_top, slab=False)
+    fi, fc = _fused(sa, q, kd, lens_t, dom, scale, k_top, slab=False)
+    torch.cuda.synchronize()
+    assert torch.equal(fc, rc), (fc.cpu(), rc.cpu())
+    assert torch.equal(fi, ri)
+    exp = np.minimum(k_top, np.repeat(np.asarray(lens), Hq)).reshape(B, Hq)
+    assert np.array_equal(fc.cpu().numpy(), exp)
+
+
 def test_token_topk_pads_wider_output(sa):
     """max_out above k_top: the selection is the same and the rest is -1."""
     q, kd, lens_t, dom = _inputs("bf16", 1, 4, 1, 12000, 16, [11000], 77)
@@ -122,6 +153,24 @@ def test_token_topk_decode_c5_shape(sa):
     fused.rope()
     fused.score_select()
     ri, rc = _two_step(sa, fused.q_rope, fused.k, fused.cache_len, fused.dom, fused.scale, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.tok_cnt, rc)
+    assert torch.equal(fused.tok_idx, ri)
+
+
+def test_token_topk_decode_c4_shape(sa):
+    """The 64K standard-layout decode workload (batch 16, top-2048), as the
+    bench runs it: the fused step's selection equals the two-step one."""
+    from long_context_sparse_apply_amd.pipeline import DecodeStep
+    import synth.device as SD
+    cfg = W.C4
+    dt = SD.decode_tensors(cfg)
+    fused = DecodeStep(dt["q_raw"], dt["k"], dt["v"], dt["lens"], dt["dom"], theta=cfg.theta,
+                       top_k=cfg.k, slab=bool(cfg.slab), k_rest=dt["k_rest"], fused=True)
+    fused.rope()
+    fused.score_select()
+    ri, rc = _two_step(sa, fused.q_rope, fused.k, fused.cache_len, fused.dom, fused.scale, cfg.k,
+                       slab=bool(cfg.slab))
     torch.cuda.synchronize()
     assert torch.equal(fused.tok_cnt, rc)
     assert torch.equal(fused.tok_idx, ri)
