@@ -757,6 +757,39 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
 #pragma unroll
       for (int hh = 0; hh < GRP; ++hh) skey[hh][j] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
     }
+  } else if constexpr (sizeof(T) == 2 && NDC <= 32) {
+    // standard rows, bf16, up to 32 scored channels: in round j a wave loads
+    // the scored channels of its 64 samples with NDC lanes a row (64 / NDC
+    // rows an instruction, so each load touches a few lines, not 64), parks
+    // the raw values in its LDS slice, and each lane then scores its own
+    // sample from there with the same sequential arithmetic
+    constexpr int RPI = kWave / NDC;           // rows an instruction
+    __shared__ uint16_t s_raw[kLongThreads / kWave][kWave][NDC];
+    const int wv = tid / kWave, ln = tid & (kWave - 1);
+    const int rsub = ln / NDC, slot = ln % NDC;
+    const int ch = s_ch[slot];
+#pragma unroll 1
+    for (int j = 0; j < KPT; ++j) {
+      uint16_t raw[kWave / RPI];
+#pragma unroll
+      for (int i = 0; i < kWave / RPI; ++i) {
+        const int e = j * kLongThreads + wv * kWave + i * RPI + rsub;  // the sample loaded
+        const int tok_e = e < nsamp ? (e / seg_len) * seg_stride + e % seg_len : 0;
+        raw[i] = reinterpret_cast<const uint16_t*>(kb)[static_cast<int64_t>(tok_e) * d + ch];
+      }
+#pragma unroll
+      for (int i = 0; i < kWave / RPI; ++i) s_raw[wv][i * RPI + rsub][slot] = raw[i];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes landed
+      __builtin_amdgcn_wave_barrier();
+      float kv[NDC];
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) kv[c] = __uint_as_float(static_cast<uint32_t>(s_raw[wv][ln][c]) << 16);
+      const bool in = tid + j * kLongThreads < nsamp;
+#pragma unroll
+      for (int hh = 0; hh < GRP; ++hh) skey[hh][j] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the slice's reads done before it is rewritten
+      __builtin_amdgcn_wave_barrier();
+    }
   } else {
     // standard rows: the scored channels of RND samples at a time
     int tok[KPT];

@@ -184,7 +184,8 @@ class DecodeCache:
 
 
 class DecodeStep:
-    """One decode step.  ``fused`` (default: the slab layout) scores and
+    """One decode step.  ``fused`` (the default for the slab layout, and for
+    the standard layout in bf16 with at most 16 dominant pairs) scores and
     selects the tokens with sa_token_topk, which writes no score array;
     otherwise sa_token_score then sa_topk_select (the same selection)."""
 
@@ -201,10 +202,12 @@ class DecodeStep:
         # position of the decoding token per batch row: cache_len - 1 (int32, [B])
         self.pos = (cache_len - 1).to(torch.int32).contiguous()
         self.q_rope = torch.empty_like(q_raw)
-        # (fused by default with the slab; with the standard layout the
-        # sampled threshold's scattered channel reads cost more than the score
-        # array it saves at the 64K shape, so two calls stay the default there)
-        self.fused = slab if fused is None else bool(fused)
+        # fused by default with the slab, and with the standard layout where
+        # its threshold reads the rows coalesced (bf16, at most 16 dominant
+        # pairs); elsewhere that threshold's scattered reads cost more than
+        # the score array saves
+        fast_std = q_raw.dtype == torch.bfloat16 and 2 * dom_pairs.shape[1] <= 32
+        self.fused = (slab or fast_std) if fused is None else bool(fused)
         if self.fused:
             self.scores = None
             self.ws_sel = torch.empty(workspace_bytes(SA_OP_TOKEN_TOPK, rows=B * Hq, cols=L,
