@@ -737,7 +737,37 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
   const int seg_step = kLongThreads / seg_len, off_step = kLongThreads % seg_len;
   int seg = tid / seg_len, off = tid % seg_len;
   uint32_t skey[GRP][KPT];
-  if constexpr (SLAB) {
+  if constexpr (SLAB && R16 <= 4) {
+    // slab rows of at most 64 bytes: in round j a wave loads its 64 samples'
+    // rows with R16 lanes a row (64 / R16 rows an instruction, so each load
+    // touches a few lines, not 64), parks them in its LDS slice, and each
+    // lane unpacks and scores its own sample from there
+    constexpr int RPI = kWave / R16;           // rows an instruction
+    __shared__ uint4 s_rows[kLongThreads / kWave][kWave][R16];
+    const int wv = tid / kWave, ln = tid & (kWave - 1);
+    const int rsub = ln / R16, part = ln % R16;
+#pragma unroll 1
+    for (int j = 0; j < KPT; ++j) {
+      uint4 raw[R16];
+#pragma unroll
+      for (int i = 0; i < R16; ++i) {
+        const int e = j * kLongThreads + wv * kWave + i * RPI + rsub;  // the sample loaded
+        const int tok_e = e < nsamp ? (e / seg_len) * seg_stride + e % seg_len : 0;
+        raw[i] = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(tok_e) * NDC)[part];
+      }
+#pragma unroll
+      for (int i = 0; i < R16; ++i) s_rows[wv][i * RPI + rsub][part] = raw[i];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes landed
+      __builtin_amdgcn_wave_barrier();
+      float kv[NDC];
+      load_slab_row<T, NDC>(reinterpret_cast<const T*>(&s_rows[wv][ln][0]), kv);
+      const bool in = tid + j * kLongThreads < nsamp;
+#pragma unroll
+      for (int hh = 0; hh < GRP; ++hh) skey[hh][j] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the slice's reads done before it is rewritten
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else if constexpr (SLAB) {
     uint4 w[KPT][R16];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
