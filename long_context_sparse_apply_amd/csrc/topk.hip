@@ -623,8 +623,8 @@ hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_
 // from the dominant chunks, then the critical subset T_t).  Three kernels:
 //  1. token_thr_kernel, one work-group per (batch, KV head): a sampled
 //     threshold for each of the group's query heads, from the scores of
-//     kSegs x kSegLenF sampled tokens (each sample's slab row read once for
-//     all heads).  Rows with k = 0 or k >= their length get a threshold
+//     kSegs x kSegLenF sampled tokens (each sample's row read once for all
+//     heads).  Rows with k = 0 or k >= their length get a threshold
 //     nothing passes, rows too short to sample one that takes every token.
 //  2. the token scoring kernel in collect mode (token_score.hip): the same
 //     scores as the scoring entry point; tokens at or above the threshold go
@@ -636,7 +636,8 @@ hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_
 //     threshold only steers how many candidates come back, so the result is
 //     the top-k of the scores whatever it is.
 // The slab row of a token is the 2 n_dom dominant channels (NDC), read as
-// 16-byte words.
+// 16-byte words; a standard row holds all d channels, of which the scored
+// ones are read through the scoring kernel's channel table.
 
 constexpr int kSegLenF = 64;                                  // samples a segment (at most)
 constexpr int kSampPerThreadF = kSegs * kSegLenF / kLongThreads;  // 8
