@@ -16,11 +16,11 @@ no criterion.  Reading taken here:
   calibration queries; the dominant set is the n_dom pairs with the largest
   counts (ties to the lower pair), listed in ascending order.
 
-The top-k decisions are integer results of floating-point scores, so they are
-taken in the precision the GPU path scores in: fp32, the full score summed
-channel by channel in ascending order, each pair score one rounding of the
-sum of its two products.  With bf16-stored inputs every product is exact in
-fp32, so these scores are fully determined.
+Every score is the plain fp64 definition above (one matrix product for the
+full scores, one sum of two products for a pair).  A fast path that scores in
+lower precision may order near-tied keys differently; comparing it with this
+definition is the test's business (it bounds that path's rounding), not the
+oracle's.
 """
 from __future__ import annotations
 
@@ -28,21 +28,20 @@ import numpy as np
 
 
 def calibration_scores(q: np.ndarray, k: np.ndarray):
-    """q [d], k [L, d] (stored values) -> (full [L], pairs [P, L]) in fp32."""
+    """q [d], k [L, d] -> (full [L], pairs [P, L]), fp64."""
     d = q.shape[-1]
     P = d // 2
-    prod = q.astype(np.float32)[None, :] * k.astype(np.float32)  # exact for bf16 inputs
-    full = np.zeros(k.shape[0], np.float32)
-    for c in range(d):
-        full = full + prod[:, c]  # float32 + float32: one rounding per channel, in order
-    pairs = (prod[:, :P] + prod[:, P:]).T
+    qd = np.asarray(q, np.float64)
+    kd = np.asarray(k, np.float64)
+    full = kd @ qd
+    pairs = (kd[:, :P] * qd[None, :P] + kd[:, P:] * qd[None, P:]).T
     return full, pairs
 
 
 def topk_set(scores: np.ndarray, k: int) -> np.ndarray:
     """Indices of the k best entries by (score descending, index ascending)."""
     idx = np.arange(scores.shape[0])
-    order = np.lexsort((idx, -scores.astype(np.float64)))
+    order = np.lexsort((idx, -np.asarray(scores, np.float64)))
     return np.sort(order[:k])
 
 
@@ -63,12 +62,18 @@ def overlap_counts(q: np.ndarray, k: np.ndarray, k_cal: int) -> np.ndarray:
     return counts
 
 
-def calibrate_dominant(q: np.ndarray, k: np.ndarray, k_cal: int, n_dom: int):
-    """-> (counts [Hkv, P], dominant pairs [Hkv, n_dom] ascending)."""
-    counts = overlap_counts(q, k, k_cal)
+def dominant_from_counts(counts: np.ndarray, n_dom: int) -> np.ndarray:
+    """counts [Hkv, P] -> the n_dom pairs with the largest counts per KV head
+    (ties to the lower pair), ascending."""
     P = counts.shape[1]
     dom = np.empty((counts.shape[0], n_dom), np.int32)
     for g in range(counts.shape[0]):
         order = np.lexsort((np.arange(P), -counts[g]))
         dom[g] = np.sort(order[:n_dom])
-    return counts, dom
+    return dom
+
+
+def calibrate_dominant(q: np.ndarray, k: np.ndarray, k_cal: int, n_dom: int):
+    """-> (counts [Hkv, P], dominant pairs [Hkv, n_dom] ascending)."""
+    counts = overlap_counts(q, k, k_cal)
+    return counts, dominant_from_counts(counts, n_dom)

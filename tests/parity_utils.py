@@ -118,3 +118,115 @@ def check_selection(gpu_sel, ref_scores, valid_len, k, n_sink, n_local, rtol=SCO
     best_dropped = np.max((s - t)[~is_kept])
     assert worst_kept >= best_dropped, "selection not threshold-consistent"
     return False
+
+
+# ----------------------------------------------------------------------------- top-k under rounding
+def count_greater(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """For each t: the number of u with (a_u, -u) > (b_t, -t), i.e. entries
+    that rank above position t's value b_t in a top-k by (value descending,
+    index ascending).  u = t is counted when a_t > b_t."""
+    n = a.shape[0]
+    idx = np.arange(n)
+    val = np.concatenate([a, b]).astype(np.float64)
+    neg = np.concatenate([-idx, -idx])
+    typ = np.concatenate([np.zeros(n, np.int64), np.ones(n, np.int64)])
+    # ascending by (value, -index, type): an a-entry equal to a b-entry sorts
+    # before it, so every a-entry after a b-entry is strictly greater
+    order = np.lexsort((typ, neg, val))
+    is_a = (typ[order] == 0).astype(np.int64)
+    a_after = is_a.sum() - np.cumsum(is_a)
+    out = np.empty(n, np.int64)
+    bpos = np.nonzero(typ[order] == 1)[0]
+    out[order[bpos] - n] = a_after[bpos]
+    return out
+
+
+def topk_status(s: np.ndarray, tol: np.ndarray, k: int):
+    """Top-k (value descending, index ascending) of scores known only to lie
+    in [s - tol, s + tol].  Returns (sure_in, ambiguous) masks: a sure_in
+    entry is in every top-k the rounded scores can give, an entry in neither
+    mask is in none, and exactly k - sure_in.sum() of the ambiguous ones are
+    chosen."""
+    s = np.asarray(s, np.float64)
+    tol = np.asarray(tol, np.float64)
+    n = s.shape[0]
+    if k >= n:
+        return np.ones(n, bool), np.zeros(n, bool)
+    lo, hi = s - tol, s + tol
+    could = count_greater(hi, lo) - (hi > lo)   # others that may rank above
+    sure = count_greater(lo, hi)                # others that rank above for certain (lo_t < hi_t)
+    sure_in = could < k
+    sure_out = sure >= k
+    assert not np.any(sure_in & sure_out)
+    return sure_in, ~(sure_in | sure_out)
+
+
+def overlap_range(f_in, f_amb, kf: int, p_in, p_amb, kp: int):
+    """Smallest and largest |F & P| over the selections F (all of f_in plus
+    kf - |f_in| of f_amb) and P (all of p_in plus kp - |p_in| of p_amb)."""
+    f_out = ~(f_in | f_amb)
+    p_out = ~(p_in | p_amb)
+    rf = kf - int(f_in.sum())
+    rp = kp - int(p_in.sum())
+    assert 0 <= rf <= int(f_amb.sum()) and 0 <= rp <= int(p_amb.sum())
+    SS = int((f_in & p_in).sum())
+    SA = int((f_in & p_amb).sum())
+    AS = int((f_amb & p_in).sum())
+    AA = int((f_amb & p_amb).sum())
+    AO = int((f_amb & p_out).sum())
+    OA = int((f_out & p_amb).sum())
+    lo_best, hi_best = None, None
+    for xa in range(min(AA, rf) + 1):
+        xs_lo, xs_hi = max(0, rf - xa - AO), min(AS, rf - xa)
+        if xs_lo > xs_hi:
+            continue
+        for ya in range(min(AA, rp) + 1):
+            ys_lo, ys_hi = max(0, rp - ya - OA), min(SA, rp - ya)
+            if ys_lo > ys_hi:
+                continue
+            z_lo, z_hi = max(0, xa + ya - AA), min(xa, ya)
+            lo = SS + xs_lo + ys_lo + z_lo
+            hi = SS + xs_hi + ys_hi + z_hi
+            lo_best = lo if lo_best is None else min(lo_best, lo)
+            hi_best = hi if hi_best is None else max(hi_best, hi)
+    assert lo_best is not None
+    return lo_best, hi_best
+
+
+# fp32 rounding of the calibration scores: the full score is a running fp32
+# sum of d exact products (bf16 x bf16), a pair score one rounding of the sum
+# of two exact products.  Recursive summation of n terms is within
+# gamma_n * sum |terms| of the exact sum, gamma_n = n u / (1 - n u), u = 2^-24.
+def gamma(n: int, u: float = 2.0 ** -24) -> float:
+    return n * u / (1.0 - n * u)
+
+
+def calibration_count_bounds(q: np.ndarray, k: np.ndarray, k_cal: int):
+    """Admissible per-pair counts [lo, hi] ([Hkv, P] each) of an fp32
+    calibration against the oracle's fp64 scores, plus the number of
+    (query, pair) overlaps that were ambiguous."""
+    from oracle import calibration as C
+    Hq, M, d = q.shape
+    Hkv, L = k.shape[:2]
+    P = d // 2
+    grp = Hq // Hkv
+    lo = np.zeros((Hkv, P), np.int64)
+    hi = np.zeros((Hkv, P), np.int64)
+    n_amb = 0
+    for h in range(Hq):
+        g = h // grp
+        ak = np.abs(k[g].astype(np.float64))
+        for m in range(M):
+            full, pairs = C.calibration_scores(q[h, m], k[g])
+            aq = np.abs(q[h, m].astype(np.float64))
+            # fp32 bound plus the fp64 oracle's own (far smaller) rounding
+            t_full = (gamma(d) + gamma(d, 2.0 ** -53)) * (ak @ aq)
+            t_pair = (gamma(2) + gamma(2, 2.0 ** -53)) * (ak[:, :P] * aq[:P] + ak[:, P:] * aq[P:]).T
+            f_in, f_amb = topk_status(full, t_full, k_cal)
+            for i in range(P):
+                p_in, p_amb = topk_status(pairs[i], t_pair[i], k_cal)
+                a, b = overlap_range(f_in, f_amb, k_cal, p_in, p_amb, k_cal)
+                lo[g, i] += a
+                hi[g, i] += b
+                n_amb += a != b
+    return lo, hi, n_amb

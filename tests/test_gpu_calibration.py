@@ -1,10 +1,17 @@
 """GPU parity of the offline calibration of the dominant rotary pairs.
 
 "FASA: Frequency-aware Sparse Attention", sec. 2.A and sec. 2.B item 1; the
-criterion is the one the oracle states (oracle/calibration.py).  The scores
-behind every top-k decision are fp32 on both sides, computed in the same
-channel order from bf16 inputs whose products are exact, so the per-pair
-counts and the dominant sets must agree bit for bit.
+criterion is the one the oracle states (oracle/calibration.py), whose scores
+are plain fp64.  The GPU scores in fp32 (a running sum of exact bf16
+products; a pair score one rounding of two products), so near the k-th and
+(k+1)-th key its top-k may differ from the oracle's.  The test bounds that:
+from the oracle's scores and the fp32 rounding bound, every key of every
+selection is sure-in, sure-out or ambiguous, and each per-query, per-pair
+overlap lies in a range that collapses to the oracle's value wherever no
+boundary is ambiguous (tests/parity_utils.calibration_count_bounds).  The
+GPU's per-pair counts must lie in the summed ranges (equal to the oracle's
+where every range is one value), and its dominant set must be the top n_dom
+of its own counts (integer work, bit for bit).
 """
 import numpy as np
 import pytest
@@ -12,7 +19,7 @@ import torch
 
 from oracle import calibration as C
 from synth import workloads as W
-from tests.parity_utils import say
+from tests.parity_utils import calibration_count_bounds, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -55,8 +62,22 @@ def test_calibration_parity(sa, name, cfg, k_cal, n_dom):
     q, k, planted = W.calibration_inputs_host(cfg)
     dom, counts = _run(sa, q, k, k_cal, n_dom)
     ref_counts, ref_dom = C.calibrate_dominant(q, k, k_cal, n_dom)
-    assert np.array_equal(counts, ref_counts), np.abs(counts - ref_counts).max()
-    assert np.array_equal(dom, ref_dom)
+    lo, hi, n_amb = calibration_count_bounds(q, k, k_cal)
+    assert np.all((lo <= ref_counts) & (ref_counts <= hi))
+    inside = (lo <= counts) & (counts <= hi)
+    assert inside.all(), (np.argwhere(~inside)[:5], counts[~inside][:5], lo[~inside][:5],
+                          hi[~inside][:5])
+    exact = lo == hi
+    assert np.array_equal(counts[exact], ref_counts[exact])
+    # the dominant set is the top n_dom of the GPU's own counts
+    assert np.array_equal(dom, C.dominant_from_counts(counts.astype(np.int64), n_dom))
+    # where the oracle's ranges separate the n_dom-th from the next, the sets are equal
+    for g in range(counts.shape[0]):
+        rest = np.setdiff1d(np.arange(counts.shape[1]), ref_dom[g])
+        if rest.size == 0 or lo[g, ref_dom[g]].min() > hi[g, rest].max():
+            assert np.array_equal(dom[g], ref_dom[g]), g
+    say(f"  counts inside the fp32 bounds; {n_amb} ambiguous (query, pair) overlaps, "
+        f"{int(exact.sum())}/{exact.size} counts fixed exactly")
     if name == "small-planted":
         assert np.array_equal(dom, planted)
     if name == "all-keys-all-pairs":
