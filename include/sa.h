@@ -182,8 +182,9 @@ sa_status sa_token_score(const void* q_rope, const void* k, const void* k_rest, 
  *   n_local = 0, idx_out, max_out, count_out).
  *   q_rope [B, Hq, d]; k: the standard cache [B, Hkv, Lmax, d] (slab = 0) or
  *   the slab [B, Hkv, Lmax, 2*n_dom] (slab = 1); cache_len, dom_pairs as in
- *   sa_token_score.  With the slab, 2*n_dom channels of dtype must take 16,
- *   32, 64 or 128 bytes (SA_ERR_UNSUPPORTED otherwise).
+ *   sa_token_score.  With the slab, 2*n_dom must be 8, 16, 32 or 64 channels
+ *   and a slab row at most 128 bytes (bf16: n_dom 4-32; fp32: n_dom 4-16);
+ *   SA_ERR_UNSUPPORTED otherwise.
  *   idx_out [B*Hq, max_out] int32 (max_out >= k_top), count_out [B*Hq].
  *   ws: sa_workspace_bytes(SA_OP_TOKEN_TOPK, B*Hq, Lmax, 0, 0, 0) bytes: per
  *   row a sampled threshold, and per row, tile of 4096 tokens and scoring
@@ -228,11 +229,30 @@ sa_status sa_topk_select(const float* scores, int64_t rows, int cols, const int3
                          size_t ws_bytes, void* stream);
 
 /*
+ * sa_prefill_row_params -- per-row arguments of sa_topk_select for the
+ * B*Hq*N block rows of a prefill layer (host helper: integer arithmetic on
+ * host memory, no device work, no stream).  Prism sec. 1 keeps a subset of
+ * the key blocks of each query block; the budget reading: query block I sees
+ * I + 1 blocks when causal (all N otherwise) and keeps keep_const blocks if
+ * keep_const > 0, else ceil(keep_percent * visible / 100) in exact integer
+ * arithmetic; forced sink and local blocks come on top of it.
+ *   N: query blocks per head (S / block); heads: B * Hq; row r = head * N + I.
+ *   valid_len_out, k_per_row_out: caller-owned host int32 arrays of heads*N
+ *   entries, each nullable (then not written).
+ * Returns the largest per-row budget (>= 0), or -SA_ERR_SHAPE (N < 1, heads
+ * < 1, heads * N above 2^31 - 1) / -SA_ERR_RANGE (keep_const < 0,
+ * keep_percent outside [0, 100], both zero).
+ */
+int sa_prefill_row_params(int N, int64_t heads, int causal, int keep_const, int keep_percent,
+                          int32_t* valid_len_out, int32_t* k_per_row_out);
+
+/*
  * sa_sparse_attn_prefill -- block-sparse softmax attention (Prism sec. 1).
  *   q_rope [B, Hq, S, d], k_rope [B, Hkv, S, d], v [B, Hkv, S, d], dtype.
  *   blk_idx [B, Hq, N, max_sel] int32: the key blocks each query block
  *   attends to (ascending, distinct, < N; entries past blk_cnt ignored);
- *   blk_cnt [B, Hq, N] int32 in [0, max_sel].
+ *   blk_cnt [B, Hq, N] int32 in [0, max_sel] (a count outside that range
+ *   is clamped to it on the device, so no read leaves the row).
  *   causal: 1 -> a query at position t sees keys s <= t only (a token mask
  *   inside the diagonal block; blocks J > I contribute nothing).
  *   out [B, Hq, S, d] dtype = softmax(sm_scale q k^T) v over the selected
@@ -263,7 +283,7 @@ sa_status sa_sparse_attn_prefill(const void* q_rope, const void* k_rope, const v
  *   memory and the selected rows of the rest are read over the host link
  *   when they are needed).
  *   tok_idx [B, Hq, max_k] int32 token positions (< cache_len[b]), tok_cnt
- *   [B, Hq] in [0, max_k].
+ *   [B, Hq] in [0, max_k] (clamped to that range on the device).
  *   cache_len is accepted for symmetry with sa_token_score and may be NULL:
  *   the selection already lies inside each cache.  Entries of tok_idx
  *   outside [0, Lmax) are skipped.  With slab == 1, n_dom must be a

@@ -24,7 +24,8 @@ SA_F32, SA_BF16 = 0, 1
 SA_OP_BLOCK_SCORE, SA_OP_TOPK, SA_OP_DECODE, SA_OP_TOKEN_TOPK = 1, 2, 3, 4
 
 EXPORTED = ("sa_rope_apply", "sa_kv_cache_append", "sa_block_score", "sa_token_score",
-            "sa_token_topk", "sa_topk_select", "sa_sparse_attn_prefill", "sa_sparse_attn_decode",
+            "sa_token_topk", "sa_topk_select", "sa_prefill_row_params", "sa_sparse_attn_prefill",
+            "sa_sparse_attn_decode",
             "sa_calibrate_dominant", "sa_calibrate_workspace_bytes", "sa_sfa_sparsify",
             "sa_workspace_bytes",
             "sa_status_string", "sa_version")
@@ -49,6 +50,7 @@ def _load() -> ctypes.CDLL:
         "sa_token_score": [P, P, P, I, I, I, I, I, I, P, P, I, I, F, P, P],
         "sa_token_topk": [P, P, I, I, I, I, I, I, P, P, I, I, F, I, P, I, P, P, SZ, P],
         "sa_topk_select": [P, I64, I, P, P, I, I, I, P, I, P, P, SZ, P],
+        "sa_prefill_row_params": [I, I64, I, I, I, P, P],
         "sa_sparse_attn_prefill": [P, P, P, I, I, I, I, I, I, I, P, P, I, I, F, P, P, P],
         "sa_sparse_attn_decode": [P, P, P, P, I, I, I, I, I, I, P, P, I, I, P, P, I, F, P, P, P,
                                   SZ, P],
@@ -358,18 +360,18 @@ def sa_sfa_sparsify(x, out, *, k_feat: int, stream=None):
 # ----------------------------------------------------------------------------- setup helpers
 def prefill_row_params(B: int, Hq: int, N: int, *, keep_const: int = 0, keep_percent: int = 0,
                        causal: bool = True, device="cuda"):
-    """Per-row arguments of sa_topk_select for the B*Hq*N prefill block rows.
-
-    Row (b, h, I) sees I + 1 blocks when causal (all N otherwise) and keeps
-    keep_const blocks, or ceil(keep_percent / 100 * (I + 1)) (exact integer
-    arithmetic).  Returns (valid_len, k_per_row, k_max) with int32 GPU
-    tensors of B*Hq*N entries; built once per shape.
-    """
+    """Per-row arguments of sa_topk_select for the B*Hq*N prefill block rows,
+    from the library's sa_prefill_row_params (the keep budget lives in the C
+    library).  Returns (valid_len, k_per_row, k_max) with int32 tensors of
+    B*Hq*N entries on ``device``; built once per shape."""
     import numpy as np
     torch = _torch()
-    I = np.arange(N, dtype=np.int64)
-    vis = I + 1 if causal else np.full(N, N, np.int64)
-    kk = np.full(N, keep_const, np.int64) if keep_const else (keep_percent * vis + 99) // 100
-    vl = np.tile(vis, B * Hq).astype(np.int32)
-    kr = np.tile(kk, B * Hq).astype(np.int32)
-    return (torch.from_numpy(vl).to(device), torch.from_numpy(kr).to(device), int(kk.max()))
+    rows = B * Hq * N
+    vl = np.empty(rows, np.int32)
+    kr = np.empty(rows, np.int32)
+    kmax = lib.sa_prefill_row_params(int(N), int(B * Hq), 1 if causal else 0, int(keep_const),
+                                     int(keep_percent), vl.ctypes.data_as(ctypes.c_void_p),
+                                     kr.ctypes.data_as(ctypes.c_void_p))
+    if kmax < 0:
+        raise SAError("sa_prefill_row_params", -kmax)
+    return torch.from_numpy(vl).to(device), torch.from_numpy(kr).to(device), int(kmax)

@@ -151,10 +151,10 @@ sa_status sa_token_topk(const void* q_rope, const void* k, sa_dtype dtype, int B
   if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return SA_ERR_UNSUPPORTED;
   if (n_dom < 1 || n_dom > d / 2 || k_top < 0 || max_out < 1 || max_out < k_top) return SA_ERR_RANGE;
   if (slab) {
-    // slab rows of 16 to 128 bytes in a power of two
-    const int row_bytes = 2 * n_dom * (dtype == SA_BF16 ? 2 : 4);
-    if (row_bytes < 16 || row_bytes > 128 || (row_bytes & (row_bytes - 1)) != 0)
-      return SA_ERR_UNSUPPORTED;
+    // slab rows of 8 to 64 channels in a power of two, at most 128 bytes
+    const int w = 2 * n_dom;
+    const int row_bytes = w * (dtype == SA_BF16 ? 2 : 4);
+    if (w < 8 || row_bytes > 128 || (w & (w - 1)) != 0) return SA_ERR_UNSUPPORTED;
   }
   const int64_t rows = static_cast<int64_t>(B) * Hq;
   if (!ws || ws_bytes < sa::token_topk_ws_bytes(rows, Lmax)) return SA_ERR_WORKSPACE;
@@ -179,6 +179,25 @@ sa_status sa_topk_select(const float* scores, int64_t rows, int cols, const int3
   if (rows > 0x7fffffffLL) return SA_ERR_SHAPE;
   return launched(sa::launch_topk(scores, rows, cols, valid_len, k_per_row, k_const, n_sink,
                                   n_local, idx_out, max_out, count_out, as_stream(stream)));
+}
+
+int sa_prefill_row_params(int N, int64_t heads, int causal, int keep_const, int keep_percent,
+                          int32_t* valid_len_out, int32_t* k_per_row_out) {
+  if (N < 1 || heads < 1 || heads > 0x7fffffffLL / N) return -SA_ERR_SHAPE;
+  if (keep_const < 0 || keep_percent < 0 || keep_percent > 100 || (!keep_const && !keep_percent))
+    return -SA_ERR_RANGE;
+  int kmax = 0;
+  for (int I = 0; I < N; ++I) {
+    const int64_t vis = causal ? I + 1 : N;
+    const int64_t k = keep_const ? keep_const : (keep_percent * vis + 99) / 100;
+    kmax = k > kmax ? static_cast<int>(k) : kmax;
+    for (int64_t h = 0; h < heads; ++h) {
+      const int64_t r = h * N + I;
+      if (valid_len_out) valid_len_out[r] = static_cast<int32_t>(vis);
+      if (k_per_row_out) k_per_row_out[r] = static_cast<int32_t>(k);
+    }
+  }
+  return kmax;
 }
 
 sa_status sa_sparse_attn_prefill(const void* q_rope, const void* k_rope, const void* v,

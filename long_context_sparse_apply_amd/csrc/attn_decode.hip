@@ -27,20 +27,9 @@
 
 namespace sa {
 
-constexpr int kDecChunk = 256;
-constexpr int kDecWaves = 4;
+// (chunk and wave counts: sa_limits.hpp; splits and workspace size: host_sizes.cpp)
 constexpr int kDecPerWave = kDecChunk / kDecWaves;
 constexpr int kChipCUs = 256;  // MI355X compute units
-
-int decode_splits(int max_k) {
-  const int s = (max_k + kDecChunk - 1) / kDecChunk;
-  return s < 1 ? 1 : s;
-}
-
-size_t decode_ws_bytes(int B, int Hq, int max_k) {
-  const size_t parts = static_cast<size_t>(B) * Hq * decode_splits(max_k);
-  return parts * (2 + 128) * sizeof(float) + 256;
-}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
@@ -63,7 +52,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const int h = bh % Hq;
   const int b = bh / Hq;
   const int g = h / (Hq / Hkv);
-  const int cnt = tok_cnt[bh];
+  // the count is clamped to the list width, so a count above it (a caller's
+  // stale buffer) never reads past the row of indices
+  const int cnt = min(max(tok_cnt[bh], 0), max_k);
 
   __shared__ int s_ch[D];
   __shared__ unsigned long long s_dmask[(D + 63) / 64];

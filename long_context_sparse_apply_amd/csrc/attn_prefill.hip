@@ -486,7 +486,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   // above the diagonal (causal) are skipped
   // read through the constant address space: the reads are uniform and become
   // scalar loads, which the vector-load counter the tile waits use does not see
-  const int cnt = ((uniform_i32p)blk_cnt)[sel0];
+  // clamped to the list width: a count above it never reads past the row
+  const int cnt = min(max(((uniform_i32p)blk_cnt)[sel0], 0), max_sel);
   const uniform_i32p sel = (uniform_i32p)(blk_idx + sel0 * max_sel);
   auto next_valid = [&](int from) {
     for (int t = from; t < cnt; ++t) {
@@ -630,7 +631,8 @@ __global__ __launch_bounds__(256) void prefill_plain_kernel(
   const int64_t sel0 = (static_cast<int64_t>(b) * Hq + h) * N + I;
   // read through the constant address space: the reads are uniform and become
   // scalar loads, which the vector-load counter the tile waits use does not see
-  const int cnt = ((uniform_i32p)blk_cnt)[sel0];
+  // clamped to the list width: a count above it never reads past the row
+  const int cnt = min(max(((uniform_i32p)blk_cnt)[sel0], 0), max_sel);
   const uniform_i32p sel = (uniform_i32p)(blk_idx + sel0 * max_sel);
 
   for (int qb = 0; qb < block; qb += QPG) {

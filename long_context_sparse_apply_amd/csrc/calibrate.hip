@@ -119,13 +119,6 @@ __global__ void calib_to_float_kernel(const uint32_t* __restrict__ c, float* __r
 
 static size_t al(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-size_t calib_ws_bytes(int Hq, int M, int L, int d, int Hkv, int kcal) {
-  const size_t rows = static_cast<size_t>(Hq) * M;
-  const size_t P = static_cast<size_t>(d) / 2;
-  return al(rows * L * 4) + al(rows * P * L * 4) + al(rows * kcal * 4) + al(rows * 4) +
-         al(rows * P * kcal * 4) + al(rows * P * 4) + al(static_cast<size_t>(Hkv) * P * 4) * 2 +
-         al(static_cast<size_t>(Hkv) * 4) + 256;
-}
 
 hipError_t launch_calibrate(const void* q, const void* k, int Hq, int Hkv, int M, int L, int d,
                             int kcal, int n_dom, int32_t* dom_out, int32_t* counts_out, void* ws,

@@ -16,13 +16,6 @@
 
 namespace sa {
 
-RopeFreq make_rope_freq(int d, double theta) {
-  RopeFreq r{};
-  const int P = d / 2;
-  for (int i = 0; i < P && i < kMaxPairs; ++i)
-    r.f[i] = std::pow(theta, -2.0 * i / d) / (2.0 * M_PI);
-  return r;
-}
 
 // ------------------------------------------------------------------ rotation only
 template <typename T, int D>

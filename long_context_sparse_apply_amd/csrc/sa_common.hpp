@@ -6,10 +6,9 @@
 #include <stdint.h>
 
 #include "sa_internal.hpp"
+#include "sa_limits.hpp"
 
 namespace sa {
-
-constexpr int kWave = 64;
 
 // ---------------------------------------------------------------- bf16 <-> fp32
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -61,6 +61,10 @@ hipError_t launch_token_collect(const void* q, const void* k, int dtype, int B, 
 
 // token scores and their top-k in one call, without a score array
 size_t token_topk_ws_bytes(int64_t rows, int Lmax);
+// long-row top-k: LDS of a work-group, candidate buffer of a row (plain and fused)
+size_t topk_lds_bytes(int cols, int cap);
+int topk_cap(int k);
+int token_topk_cap(int k);
 hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
                              int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
                              int n_dom, int slab, float scale, int k_top, int32_t* idx_out,

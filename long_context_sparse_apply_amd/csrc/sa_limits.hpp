@@ -1,0 +1,29 @@
+// Sizes shared by the kernels and the host-side size arithmetic (plain C++,
+// no device code), so the workspace and LDS sizes the host computes and the
+// layouts the kernels assume come from one definition.
+#pragma once
+
+namespace sa {
+
+constexpr int kWave = 64;  // wavefront width on gfx950
+
+// split-K decode attention: tokens per work-group chunk, waves per work-group
+constexpr int kDecChunk = 256;
+constexpr int kDecWaves = 4;
+
+// long-row top-k: threads per row, radix digit, largest LDS candidate
+// buffer (64-bit composites), longest row the host accepts
+constexpr int kLongThreads = 512;
+constexpr int kDigit = 11;
+constexpr int kBins = 1 << kDigit;
+constexpr int kMaxCap = 8192;
+constexpr int kMaxLongCols = 262144;
+
+// candidate lists of the fused token top-k: tokens a scoring tile covers,
+// waves of a scoring work-group (one private list each per row), entries a
+// list keeps
+constexpr int kCollectTile = 4096;
+constexpr int kCollectWaves = 4;
+constexpr int kCollectSlots = 256;
+
+}  // namespace sa

@@ -120,11 +120,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ long rows
-constexpr int kLongThreads = 512;
-constexpr int kDigit = 11;
-constexpr int kBins = 1 << kDigit;
-constexpr int kMaxCap = 8192;         // largest LDS candidate buffer (64-bit composites)
-constexpr int kMaxLongCols = 262144;  // longest row (the host rejects longer ones)
+// (threads a row, radix digit, candidate and row limits: sa_limits.hpp)
 constexpr int kSegs = 64;             // sample segments per row
 constexpr int kSegLen = 256;          // samples per segment (at most)
 constexpr int kCollectVec = 4;        // float4 loads a thread per batch of the collect pass
@@ -172,10 +168,6 @@ struct TopkShared {
   int cap;
 };
 
-size_t topk_lds_bytes(int cols, int cap) {
-  const size_t words = (static_cast<size_t>(cols) + 31) / 32;
-  return static_cast<size_t>(cap) * 8 + kBins * 4 + words * 4 + (kLongThreads / kWave + 4) * 4;
-}
 
 __device__ __forceinline__ TopkShared topk_views(uint8_t* lds, int cols, int cap) {
   TopkShared sh;
@@ -581,13 +573,6 @@ __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
   emit_bitmap(sh, nwords, idx_out + row * max_out, max_out, count_out + row);
 }
 
-// Candidate buffer of a long row: k plus a quarter plus 1024 (the sampled
-// threshold overshoots k by a few standard deviations), at most kMaxCap.
-int topk_cap(int k) {
-  int cap = k + k / 4 + 1024;
-  cap = ((cap + 63) / 64) * 64;
-  return cap > kMaxCap ? kMaxCap : cap;
-}
 
 hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_t* valid_len,
                        const int32_t* k_per_row, int k_const, int n_sink, int n_local,
@@ -642,14 +627,6 @@ hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_
 constexpr int kSegLenF = 64;                                  // samples a segment (at most)
 constexpr int kSampPerThreadF = kSegs * kSegLenF / kLongThreads;  // 8
 
-// A row's candidate buffer in the fused selection: twice k plus 1024 (a
-// threshold sampled from kSegs x kSegLenF tokens overshoots k by more), at
-// most kMaxCap.
-int token_topk_cap(int k) {
-  int cap = 2 * k + 1024;
-  cap = ((cap + 63) / 64) * 64;
-  return cap > kMaxCap ? kMaxCap : cap;
-}
 
 // The scaled dominant query slice of row `row` in slab channel order, as the
 // scoring kernel stages it: thread t < NDC writes channel t.
@@ -963,14 +940,10 @@ __global__ __launch_bounds__(kLongThreads) void token_select_kernel(
   emit_bitmap(sh, nwords, idx_out + row * max_out, max_out, count_out + row);
 }
 
-// Workspace: thresholds [rows], list counts [rows, tiles, waves] and lists
-// [rows, tiles, waves, kCollectSlots], each part 256-byte aligned.
+// Workspace (sized by token_topk_ws_bytes): thresholds [rows], list counts
+// [rows, tiles, waves] and lists [rows, tiles, waves, kCollectSlots], each
+// part 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-size_t token_topk_ws_bytes(int64_t rows, int Lmax) {
-  const size_t tiles = static_cast<size_t>((Lmax + kCollectTile - 1) / kCollectTile);
-  const size_t lists = static_cast<size_t>(rows) * tiles * kCollectWaves;
-  return align256(static_cast<size_t>(rows) * 4) + align256(lists * 4) + lists * kCollectSlots * 8;
-}
 
 hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
                              int Lmax, int d, const int32_t* cache_len, const int32_t* dom,

@@ -50,9 +50,6 @@ constexpr uint32_t kNoCandidates = 0xffffffffu;
 // tile, wave) the number of qualifying tokens (it may exceed the slots: the
 // selection then reads the row again) and the first kCollectSlots of them as
 // score bits << 32 | token (the selection forms the composites).
-constexpr int kCollectTile = 4096;
-constexpr int kCollectWaves = 4;
-constexpr int kCollectSlots = 256;
 struct TokenCollect {
   const uint32_t* thr;  // [rows] threshold keys
   int* cnt;             // [rows, tiles, kCollectWaves]

@@ -26,6 +26,7 @@ GPU path each apply their own rotation to whatever is stored.
 from __future__ import annotations
 
 import dataclasses
+import functools
 from dataclasses import dataclass
 
 import numpy as np
@@ -334,6 +335,32 @@ def decode_inputs_host(cfg: DecodeConfig, batches=None, kv_heads=None):
             k[batches.index(b), h // cfg.group, p] = row
     return dict(q_raw=q, k=k, v=v, lens=lens_all[batches], dom=dominant_pairs(cfg),
                 batches=batches)
+
+
+def decode_cache_values(cfg: DecodeConfig, tid: int, b: int, g: int, rows, channels=None):
+    """Stored values of cache tensor ``tid`` (TID_K or TID_V, standard layout)
+    at rows ``rows`` and channels ``channels`` (default: all) of batch row b,
+    KV head g, as fp32 [len(rows), len(channels)], needle keys included.
+
+    The generator is counter-based, so a sampled check of a large cache can
+    regenerate just the elements it reads."""
+    rows = np.asarray(rows, dtype=np.int64)
+    ch = np.arange(cfg.d, dtype=np.int64) if channels is None else np.asarray(channels, np.int64)
+    base = (b * cfg.Hkv + g) * cfg.L * cfg.d
+    n = (base + rows[:, None] * cfg.d + ch[None, :]).astype(np.uint64)
+    z = gaussian_f32(cfg.seed, tid, n)
+    out = round_to_bf16(z) if cfg.dtype == "bf16" else z.astype(np.float32)
+    if tid == TID_K:
+        where = {int(t): j for j, t in enumerate(rows.tolist())}
+        for bb, h, p, row in _decode_patches_cached(cfg):
+            if bb == b and h // cfg.group == g and p in where:
+                out[where[p]] = row[ch]
+    return out
+
+
+@functools.lru_cache(maxsize=4)
+def _decode_patches_cached(cfg: DecodeConfig):
+    return decode_patches(cfg, cache_lengths(cfg))
 
 
 def decode_patches(cfg: DecodeConfig, lens: np.ndarray):

@@ -193,3 +193,26 @@ def test_prefill_row_params_budget():
     vl, kr, kmax = sa.prefill_row_params(1, 2, 256, keep_percent=10, device="cpu")
     assert vl.shape[0] == 512 and int(vl[0]) == 1 and int(vl[255]) == 256 and int(vl[256]) == 1
     assert int(kr[9]) == 1 and int(kr[10]) == 2 and int(kr[255]) == 26 and kmax == 26
+
+
+def test_prefill_row_params_match_the_oracle_budget():
+    """The library's keep budget (host helper of the C ABI) equals the
+    oracle's exact-rational ceil(p (I + 1) / 100) on every row, for the
+    32K and 128K layers and a constant budget; errors come back negative."""
+    import numpy as np
+    import long_context_sparse_apply_amd as sa
+    from oracle import sparse_attention as O
+    for N, kc, kp in ((256, 0, 10), (1024, 0, 5), (8, 4, 0), (77, 0, 33), (5, 0, 100)):
+        vl, kr, kmax = sa.prefill_row_params(2, 3, N, keep_const=kc, keep_percent=kp, device="cpu")
+        want = np.array(O.keep_budget(N, keep_const=kc, keep_percent=kp))
+        assert np.array_equal(kr.numpy(), np.tile(want, 6)) and kmax == want.max()
+        assert np.array_equal(vl.numpy(), np.tile(np.arange(1, N + 1), 6))
+    vl, kr, _ = sa.prefill_row_params(1, 1, 10, keep_percent=10, causal=False, device="cpu")
+    assert bool((vl == 10).all()) and bool((kr == 1).all())
+    L = sa.lib
+    assert L.sa_prefill_row_params(0, 4, 1, 0, 10, None, None) == -sa.SA_ERR_SHAPE
+    assert L.sa_prefill_row_params(1 << 20, 1 << 12, 1, 0, 10, None, None) == -sa.SA_ERR_SHAPE
+    assert L.sa_prefill_row_params(8, 4, 1, 0, 0, None, None) == -sa.SA_ERR_RANGE
+    assert L.sa_prefill_row_params(8, 4, 1, 0, 101, None, None) == -sa.SA_ERR_RANGE
+    assert L.sa_prefill_row_params(8, 4, 1, -1, 0, None, None) == -sa.SA_ERR_RANGE
+    assert L.sa_prefill_row_params(8, 4, 1, 3, 0, None, None) == 3

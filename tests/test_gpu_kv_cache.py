@@ -22,7 +22,7 @@ import synth
 from oracle import sparse_attention as O
 from synth import workloads as W
 from tests.parity_utils import rotated_bounds, say
-from tests.test_gpu_end_to_end import _compare_decode, _compare_prefill, _layer
+from tests.test_gpu_end_to_end import _HostCache, _all_samples, _compare_decode, _compare_prefill, _layer
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -236,9 +236,9 @@ def test_prefill_decode_handoff(sa, slab, host_rest):
         # the oracle's cache: its own rotation, stored in bf16
         k_or = synth.round_to_bf16(hc.k).astype(np.float64)
         lo, hi = hc.bounds("bf16")
-        x = dict(q_raw=q_new, k=k_or, v=hc.v, lens=lens, dom=dom)
+        x = dict(q_raw=q_new, k=k_or, v=hc.v, lens=lens, dom=dom, batches=list(range(B)))
         say(f"  step {t}: lens {lens.tolist()}")
-        _compare_decode(dcfg, step, x, list(range(B)), list(range(Hkv)), k_amb=hi - lo)
+        _compare_decode(dcfg, step, _HostCache(dcfg, x), _all_samples(dcfg, range(B)), k_amb=hi - lo)
     _check_cache(cache.k, cache.k_rest, cache.v, hc, "bf16", dom, slab)
 
 
@@ -268,4 +268,4 @@ def test_decode_host_placement(sa):
     assert torch.equal(host_step.tok_idx, dev_step.tok_idx)
     assert torch.equal(host_step.out, dev_step.out)
     assert torch.equal(host_step.lse, dev_step.lse)
-    _compare_decode(cfg, host_step, x, list(range(cfg.B)), list(range(cfg.Hkv)))
+    _compare_decode(cfg, host_step, _HostCache(cfg, x), _all_samples(cfg, range(cfg.B)))

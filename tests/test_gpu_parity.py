@@ -4,7 +4,10 @@ seeded inputs.  Needs an MI355X; every call goes through the C ABI.
 Staged tests feed both sides the same stored inputs (the same index lists for
 the attention stages, drawn from a seeded numpy generator); the end-to-end
 tests run the whole path on each side and compare scores, selections and the
-attention of rows whose selections agree.
+attention over the GPU's own selection.  Every output is carved from a
+guarded allocation (tests/guards.py) whose bands are checked after each call,
+and the selection and attention stages are run twice and must repeat bit for
+bit.
 """
 import numpy as np
 import pytest
@@ -13,6 +16,7 @@ import torch
 import synth
 from oracle import sparse_attention as O
 from synth import workloads as W
+from tests.guards import check_all, guarded
 from tests.parity_utils import LSE_ATOL_BF16, OUT_ATOL, assert_scores_close, check_selection, say
 
 pytestmark = pytest.mark.gpu
@@ -75,10 +79,11 @@ def test_rope_apply(sa, dtype, d, pos0, use_pos):
     x = _stored((B, H, S, d), dtype, 1)
     pos = np.stack([np.arange(S) * 3277 + b for b in range(B)]).astype(np.int32) if use_pos else None
     xt = _dev(x, dtype)
-    out = torch.empty_like(xt)
+    out, g_out = guarded(xt.shape, xt.dtype)
     sa.sa_rope_apply(xt, out, theta, pos=None if pos is None else torch.from_numpy(pos.ravel()).to(DEV),
                      pos0=pos0)
     torch.cuda.synchronize()
+    g_out.check("rope out")
     ref = np.empty((B, H, S, d))
     for b in range(B):
         p = pos[b] if use_pos else pos0 + np.arange(S)
@@ -111,16 +116,19 @@ def test_block_score(sa, name, cfg, _):
     q, k, v, _h = W.prefill_inputs_host(cfg)
     qt, kt = _dev(q, cfg.dtype), _dev(k, cfg.dtype)
     N = cfg.N
-    scores = torch.empty((cfg.B, cfg.Hq, N, N), dtype=torch.float32, device=DEV)
-    pq = torch.empty((cfg.B, cfg.Hq, N, cfg.d), dtype=torch.float32, device=DEV)
-    pk = torch.empty((cfg.B, cfg.Hkv, N, cfg.d), dtype=torch.float32, device=DEV)
-    qr, kr = torch.empty_like(qt), torch.empty_like(kt)
+    scores, g_s = guarded((cfg.B, cfg.Hq, N, N), torch.float32)
+    pq, g_pq = guarded((cfg.B, cfg.Hq, N, cfg.d), torch.float32)
+    pk, g_pk = guarded((cfg.B, cfg.Hkv, N, cfg.d), torch.float32)
+    qr, g_qr = guarded(qt.shape, qt.dtype)
+    kr, g_kr = guarded(kt.shape, kt.dtype)
     scale = cfg.d ** -0.5
     sa.sa_block_score(qt, kt, scores, theta=cfg.theta, block=cfg.block,
                       band_split_pair=cfg.band_split_pair, calibrate=bool(cfg.calibrate),
                       sm_scale=scale, causal=True, q_rope_out=qr, k_rope_out=kr,
                       pooled_q_out=pq, pooled_k_out=pk)
     torch.cuda.synchronize()
+    check_all(("scores", g_s), ("pooled q", g_pq), ("pooled k", g_pk), ("rotated q", g_qr),
+              ("rotated k", g_kr))
     pos = np.arange(cfg.S)
     q_rot = O.rope(q.astype(np.float64), pos, cfg.theta)
     k_rot = O.rope(k.astype(np.float64), pos, cfg.theta)
@@ -139,13 +147,14 @@ def test_block_score(sa, name, cfg, _):
         else:
             assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
     # workspace variant (pooled outputs not requested) gives identical scores
-    ws = torch.empty(sa.workspace_bytes(sa.SA_OP_BLOCK_SCORE, cfg.B * (cfg.Hq + cfg.Hkv) * N, cfg.d),
-                     dtype=torch.uint8, device=DEV)
-    s2 = torch.empty_like(scores)
+    ws, g_ws = guarded((sa.workspace_bytes(sa.SA_OP_BLOCK_SCORE, cfg.B * (cfg.Hq + cfg.Hkv) * N,
+                                           cfg.d),), torch.uint8)
+    s2, g_s2 = guarded(scores.shape, scores.dtype)
     sa.sa_block_score(qt, kt, s2, theta=cfg.theta, block=cfg.block,
                       band_split_pair=cfg.band_split_pair, calibrate=bool(cfg.calibrate),
                       sm_scale=scale, causal=True, ws=ws)
     torch.cuda.synchronize()
+    check_all(("workspace", g_ws), ("scores (workspace variant)", g_s2))
     assert torch.equal(s2, scores)
 
 
@@ -221,13 +230,19 @@ def test_topk_bit_exact(sa, case):
         vl[0] = cols
     kr = g.integers(0, kc + 1, rows).astype(np.int32) if per_k else np.full(rows, kc, np.int32)
     max_out = ns + nl + kc
-    idx = torch.full((rows, max_out), 12345, dtype=torch.int32, device=DEV)
-    cnt = torch.empty((rows,), dtype=torch.int32, device=DEV)
-    sa.sa_topk_select(torch.from_numpy(s).to(DEV), idx, cnt, k_const=kc,
-                      valid_len=torch.from_numpy(vl).to(DEV) if per_vl else None,
-                      k_per_row=torch.from_numpy(kr).to(DEV) if per_k else None,
-                      n_sink=ns, n_local=nl)
-    torch.cuda.synchronize()
+    st = torch.from_numpy(s).to(DEV)
+    runs = []
+    for rep in range(2):  # a second call must repeat the first bit for bit
+        idx, g_i = guarded((rows, max_out), torch.int32)
+        cnt, g_c = guarded((rows,), torch.int32)
+        sa.sa_topk_select(st, idx, cnt, k_const=kc,
+                          valid_len=torch.from_numpy(vl).to(DEV) if per_vl else None,
+                          k_per_row=torch.from_numpy(kr).to(DEV) if per_k else None,
+                          n_sink=ns, n_local=nl)
+        torch.cuda.synchronize()
+        check_all(("idx", g_i), ("count", g_c))
+        runs.append((idx, cnt))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
     gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
     for r in range(rows):
         ref = O.select_row(s[r].astype(np.float64), int(vl[r]), int(kr[r]), ns, nl)
@@ -290,13 +305,19 @@ def test_sparse_attn_prefill(sa, case):
                     cnt[b, h, I] = I + 1
     else:
         idx, cnt, sel = _random_selection(B, Hq, N, max_sel, S + Hq, causal, empty)
-    out = torch.empty((B, Hq, S, d), dtype=_dt(dtype), device=DEV)
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
     scale = d ** -0.5
-    sa.sa_sparse_attn_prefill(_dev(q, dtype), _dev(k, dtype), _dev(v, dtype),
-                              torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV), out,
-                              block=block, sm_scale=scale, causal=causal, lse=lse)
-    torch.cuda.synchronize()
+    qd, kd, vd = _dev(q, dtype), _dev(k, dtype), _dev(v, dtype)
+    idx_d, cnt_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV)
+    runs = []
+    for rep in range(2):  # a second call must repeat the first bit for bit
+        out, g_o = guarded((B, Hq, S, d), _dt(dtype))
+        lse, g_l = guarded((B, Hq, S), torch.float32)
+        sa.sa_sparse_attn_prefill(qd, kd, vd, idx_d, cnt_d, out, block=block, sm_scale=scale,
+                                  causal=causal, lse=lse)
+        torch.cuda.synchronize()
+        check_all(("out", g_o), ("lse", g_l))
+        runs.append((out, lse))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
     ref, rlse = O.prefill_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
                                     sel, block, scale, causal)
     got = _host(out)
@@ -335,13 +356,14 @@ def test_sparse_attn_prefill_base2(sa, case):
     k = synth.round_to_bf16(_stored((B, Hkv, S, d), "bf16", 22) * ramp)
     v = _stored((B, Hkv, S, d), "bf16", 23)
     idx, cnt, sel = _random_selection(B, Hq, N, max_sel, S + Hq + 7, causal, empty)
-    out = torch.empty((B, Hq, S, d), dtype=torch.bfloat16, device=DEV)
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    out, g_o = guarded((B, Hq, S, d), torch.bfloat16)
+    lse, g_l = guarded((B, Hq, S), torch.float32)
     ln2 = float(np.float32(np.log(2.0)))
     sa.sa_sparse_attn_prefill(_dev(q, "bf16"), _dev(k, "bf16"), _dev(v, "bf16"),
                               torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV), out,
                               block=block, sm_scale=ln2, causal=causal, lse=lse)
     torch.cuda.synchronize()
+    check_all(("out", g_o), ("lse", g_l))
     ref, rlse = O.prefill_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
                                     sel, block, ln2, causal)
     err = np.abs(_host(out) - ref).max()
@@ -386,7 +408,7 @@ def test_token_score(sa, case):
     q_store = synth.round_to_bf16(q_rot) if dtype == "bf16" else q_rot.astype(np.float32)
     kf = x["k"].astype(np.float64)
     ref = O.token_scores(q_store.astype(np.float64), kf, x["dom"], x["lens"], d ** -0.5)
-    scores = torch.empty((B, Hq, L), dtype=torch.float32, device=DEV)
+    scores, g_s = guarded((B, Hq, L), torch.float32)
     dom_t = torch.from_numpy(x["dom"]).to(DEV)
     if slab:
         kd, _kr = O.standard_to_slab(x["k"], x["dom"])
@@ -396,6 +418,7 @@ def test_token_score(sa, case):
     sa.sa_token_score(_dev(q_store, dtype), ktensor, scores, torch.from_numpy(x["lens"]).to(DEV),
                       dom_t, sm_scale=d ** -0.5, slab=bool(slab))
     torch.cuda.synchronize()
+    g_s.check("scores")
     assert_scores_close(_host(scores), ref)
 
 
@@ -430,10 +453,7 @@ def test_sparse_attn_decode(sa, case):
             sel[b][h] = t
     ref, rlse = O.decode_attention(q.astype(np.float64), x["k"].astype(np.float64),
                                    x["v"].astype(np.float64), sel, d ** -0.5)
-    out = torch.empty((B, Hq, d), dtype=_dt(dtype), device=DEV)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
-    ws = torch.empty(sa.workspace_bytes(sa.SA_OP_DECODE, B=B, Hq=Hq, max_k=max_k),
-                     dtype=torch.uint8, device=DEV)
+    ws, g_ws = guarded((sa.workspace_bytes(sa.SA_OP_DECODE, B=B, Hq=Hq, max_k=max_k),), torch.uint8)
     kw = {}
     if slab:
         kd, kr = O.standard_to_slab(x["k"], x["dom"])
@@ -441,11 +461,19 @@ def test_sparse_attn_decode(sa, case):
         kw["dom_pairs"] = torch.from_numpy(x["dom"]).to(DEV)
     else:
         ktensor = _dev(x["k"], dtype)
-    sa.sa_sparse_attn_decode(_dev(q, dtype), ktensor, _dev(x["v"], dtype),
-                             torch.from_numpy(tok).to(DEV), torch.from_numpy(cnt).to(DEV), out, ws,
-                             sm_scale=d ** -0.5, cache_len=torch.from_numpy(x["lens"]).to(DEV),
-                             slab=bool(slab), lse=lse, **kw)
-    torch.cuda.synchronize()
+    qd, vd = _dev(q, dtype), _dev(x["v"], dtype)
+    tok_d, cnt_d = torch.from_numpy(tok).to(DEV), torch.from_numpy(cnt).to(DEV)
+    runs = []
+    for rep in range(2):  # a second call must repeat the first bit for bit
+        out, g_o = guarded((B, Hq, d), _dt(dtype))
+        lse, g_l = guarded((B, Hq), torch.float32)
+        sa.sa_sparse_attn_decode(qd, ktensor, vd, tok_d, cnt_d, out, ws, sm_scale=d ** -0.5,
+                                 cache_len=torch.from_numpy(x["lens"]).to(DEV), slab=bool(slab),
+                                 lse=lse, **kw)
+        torch.cuda.synchronize()
+        check_all(("out", g_o), ("lse", g_l), ("workspace", g_ws))
+        runs.append((out, lse))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
     err = np.abs(_host(out) - ref).max()
     say(f"  max |out - ref| = {err:.3e}")
     assert err <= OUT_ATOL[dtype]
@@ -453,3 +481,64 @@ def test_sparse_attn_decode(sa, case):
     fin = np.isfinite(rlse)
     assert np.array_equal(np.isfinite(gl), fin)
     assert np.abs(gl[fin] - rlse[fin]).max() <= (1e-4 if dtype == "f32" else 1e-2)
+
+
+# ----------------------------------------------------------------------------- count clamping
+@pytest.mark.parametrize("dtype,block", [("bf16", 128), ("f32", 64)], ids=["bf16-mfma", "f32-plain"])
+def test_prefill_count_above_width_is_clamped(sa, dtype, block):
+    """blk_cnt above max_sel (a caller's stale buffer) is clamped on the
+    device to max_sel, and a negative count to 0: the output equals the one
+    with the count at the width, bit for bit, and a clamped-empty row gives
+    out = 0, lse = -inf.  The lists sit in a guarded allocation, so even an
+    unclamped read would stay inside it."""
+    say(f"case: prefill count clamping {dtype} block {block}")
+    B, Hq, Hkv, S, d, max_sel = 1, 2, 1, 1024, 128, 4
+    N = S // block
+    q = _stored((B, Hq, S, d), dtype, 41)
+    k = _stored((B, Hkv, S, d), dtype, 42)
+    v = _stored((B, Hkv, S, d), dtype, 43)
+    idx, _cnt, _sel = _random_selection(B, Hq, N, max_sel, 5, True, False)
+    qd, kd, vd = _dev(q, dtype), _dev(k, dtype), _dev(v, dtype)
+    idx_d, g_idx = guarded(idx.shape, torch.int32)
+    idx_d.copy_(torch.from_numpy(idx))
+    full = np.array([[[min(max_sel, int((idx[0, h, I] >= 0).sum())) for I in range(N)]
+                      for h in range(Hq)]], np.int32)
+    outs = []
+    for cnt in (full, np.where(full == max_sel, max_sel + 1000, full).astype(np.int32),
+                np.full_like(full, -3)):
+        out, g_o = guarded((B, Hq, S, d), _dt(dtype))
+        lse, g_l = guarded((B, Hq, S), torch.float32)
+        sa.sa_sparse_attn_prefill(qd, kd, vd, idx_d, torch.from_numpy(cnt).to(DEV), out,
+                                  block=block, sm_scale=d ** -0.5, causal=True, lse=lse)
+        torch.cuda.synchronize()
+        check_all(("out", g_o), ("lse", g_l), ("idx", g_idx))
+        outs.append((out, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert bool((outs[2][0] == 0).all()) and bool(torch.isneginf(outs[2][1]).all())
+
+
+@pytest.mark.parametrize("B,Hq", [(2, 8), (16, 32)], ids=["split-k", "one-pass"])
+def test_decode_count_above_width_is_clamped(sa, B, Hq):
+    """tok_cnt above max_k is clamped on the device to max_k (negative to 0)."""
+    say(f"case: decode count clamping B={B} Hq={Hq}")
+    dtype, Hkv, L, d, max_k = "bf16", 8 if Hq == 32 else 2, 1500, 128, 600
+    cfg, x = _decode_case_inputs(dtype, B, Hq, Hkv, L, d, 16, 0, 44)
+    q = _stored((B, Hq, d), dtype, 45)
+    g = np.random.default_rng(46)
+    tok = np.stack([[np.sort(g.choice(L, size=max_k, replace=False)) for _ in range(Hq)]
+                    for _ in range(B)]).astype(np.int32)
+    tok_d, g_tok = guarded(tok.shape, torch.int32)
+    tok_d.copy_(torch.from_numpy(tok))
+    ws, g_ws = guarded((sa.workspace_bytes(sa.SA_OP_DECODE, B=B, Hq=Hq, max_k=max_k),), torch.uint8)
+    qd, kd, vd = _dev(q, dtype), _dev(x["k"], dtype), _dev(x["v"], dtype)
+    outs = []
+    for c in (max_k, max_k + 77, -1):
+        cnt = torch.full((B, Hq), c, dtype=torch.int32, device=DEV)
+        out, g_o = guarded((B, Hq, d), torch.bfloat16)
+        lse, g_l = guarded((B, Hq), torch.float32)
+        sa.sa_sparse_attn_decode(qd, kd, vd, tok_d, cnt, out, ws, sm_scale=d ** -0.5, lse=lse)
+        torch.cuda.synchronize()
+        check_all(("out", g_o), ("lse", g_l), ("workspace", g_ws), ("tok_idx", g_tok))
+        outs.append((out, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert bool((outs[2][0] == 0).all()) and bool(torch.isneginf(outs[2][1]).all())

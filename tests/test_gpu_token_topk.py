@@ -17,6 +17,7 @@ import torch
 
 import synth
 from synth import workloads as W
+from tests.guards import check_all, guarded
 from tests.parity_utils import say
 
 pytestmark = pytest.mark.gpu
@@ -49,11 +50,13 @@ def _fused(sa, q_rope, k_dom, lens, dom, scale, k_top, max_out=None, slab=True):
     B, Hq, _ = q_rope.shape
     Lmax = k_dom.shape[2]
     max_out = k_top if max_out is None else max_out
-    ws = torch.empty(sa.workspace_bytes(sa.SA_OP_TOKEN_TOPK, rows=B * Hq, cols=Lmax, max_k=k_top),
-                     dtype=torch.uint8, device=DEV)
-    idx = torch.full((B, Hq, max_out), 12345, dtype=torch.int32, device=DEV)
-    cnt = torch.full((B, Hq), 12345, dtype=torch.int32, device=DEV)
+    ws, g_ws = guarded((sa.workspace_bytes(sa.SA_OP_TOKEN_TOPK, rows=B * Hq, cols=Lmax,
+                                           max_k=k_top),), torch.uint8)
+    idx, g_i = guarded((B, Hq, max_out), torch.int32)
+    cnt, g_c = guarded((B, Hq), torch.int32)
     sa.sa_token_topk(q_rope, k_dom, lens, dom, idx, cnt, ws, sm_scale=scale, k_top=k_top, slab=slab)
+    torch.cuda.synchronize()
+    check_all(("workspace", g_ws), ("idx", g_i), ("count", g_c))
     return idx, cnt
 
 
@@ -94,6 +97,9 @@ def test_token_topk_equals_score_then_select(sa, case):
     torch.cuda.synchronize()
     assert torch.equal(fc, rc), (fc.cpu(), rc.cpu())
     assert torch.equal(fi, ri)
+    # a second call repeats the first bit for bit
+    fi2, fc2 = _fused(sa, q, kd, lens_t, dom, scale, k_top)
+    assert torch.equal(fi2, fi) and torch.equal(fc2, fc)
     # counts are min(k, length): a row never loses a selected token
     exp = np.minimum(k_top, np.repeat(np.asarray(lens), Hq)).reshape(B, Hq)
     assert np.array_equal(fc.cpu().numpy(), exp)
