@@ -303,6 +303,29 @@ sa_status sa_sparse_attn_decode(const void* q_rope, const void* k, const void* k
                                 float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sa_sparse_attn_decode_static -- sa_sparse_attn_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same kernels and results,
+ * with the split-K partials kept in a fixed array of 16 MiB per GPU inside
+ * the library (held until the process ends) instead of a workspace argument.
+ * Makes no hipMalloc / hipFree or other allocating call.
+ *   Arguments as in sa_sparse_attn_decode without ws / ws_bytes.
+ *   The partials needed (0 when B * Hq >= 512, the one-pass form; else
+ *   B * Hq * ceil(max_k / 256) * 520 bytes) must fit the array:
+ *   SA_ERR_WORKSPACE otherwise.  Every call on a GPU shares that GPU's
+ *   array, so calls that overlap on one GPU (several streams or threads)
+ *   race; serialise them.
+ * Errors: as sa_sparse_attn_decode; SA_ERR_HIP if the array's device address
+ *         cannot be obtained.
+ */
+sa_status sa_sparse_attn_decode_static(const void* q_rope, const void* k, const void* k_rest,
+                                       const void* v, sa_dtype dtype, int B, int Hq, int Hkv,
+                                       int Lmax, int d, const int32_t* cache_len,
+                                       const int32_t* dom_pairs, int n_dom, int slab,
+                                       const int32_t* tok_idx, const int32_t* tok_cnt, int max_k,
+                                       float sm_scale, void* out, float* lse, void* stream);
+
+/*
  * sa_calibrate_dominant -- one-time offline calibration of the dominant
  * rotary pairs of every KV head.  FASA sec. 2.A (a small fixed set of
  * dominant frequency chunks reproduces a head's context selection) and sec.

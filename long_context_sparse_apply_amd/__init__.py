@@ -25,7 +25,7 @@ SA_OP_BLOCK_SCORE, SA_OP_TOPK, SA_OP_DECODE, SA_OP_TOKEN_TOPK = 1, 2, 3, 4
 
 EXPORTED = ("sa_rope_apply", "sa_kv_cache_append", "sa_block_score", "sa_token_score",
             "sa_token_topk", "sa_topk_select", "sa_prefill_row_params", "sa_sparse_attn_prefill",
-            "sa_sparse_attn_decode",
+            "sa_sparse_attn_decode", "sa_sparse_attn_decode_static",
             "sa_calibrate_dominant", "sa_calibrate_workspace_bytes", "sa_sfa_sparsify",
             "sa_workspace_bytes",
             "sa_status_string", "sa_version")
@@ -54,6 +54,8 @@ def _load() -> ctypes.CDLL:
         "sa_sparse_attn_prefill": [P, P, P, I, I, I, I, I, I, I, P, P, I, I, F, P, P, P],
         "sa_sparse_attn_decode": [P, P, P, P, I, I, I, I, I, I, P, P, I, I, P, P, I, F, P, P, P,
                                   SZ, P],
+        "sa_sparse_attn_decode_static": [P, P, P, P, I, I, I, I, I, I, P, P, I, I, P, P, I, F, P,
+                                         P, P],
         "sa_calibrate_dominant": [P, P, I, I, I, I, I, I, I, I, P, P, P, SZ, P],
         "sa_calibrate_workspace_bytes": [I, I, I, I, I, I],
         "sa_sfa_sparsify": [P, P, I, I64, I, I, P],
@@ -319,6 +321,31 @@ def sa_sparse_attn_decode(q_rope, k, v, tok_idx, tok_cnt, out, ws, *, sm_scale: 
           _dtype_code(q_rope), B, Hq, Hkv, Lmax, d, _ptr(cache_len), _ptr(dom_pairs), n_dom,
           int(bool(slab)), _ptr(tok_idx), _ptr(tok_cnt), tok_idx.shape[-1], float(sm_scale),
           _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream))
+    return out
+
+
+def sa_sparse_attn_decode_static(q_rope, k, v, tok_idx, tok_cnt, out, *, sm_scale: float,
+                                 cache_len=None, dom_pairs=None, slab: bool = False, k_rest=None,
+                                 lse=None, stream=None):
+    """sa_sparse_attn_decode without a workspace: the split-K partials live in
+    the library's fixed per-GPU array (no allocation; calls that overlap on
+    one GPU race)."""
+    torch = _torch()
+    _check(q_rope, "q_rope", ndim=3)
+    _check(k, "k", q_rope.dtype, 4)
+    _check(k_rest, "k_rest", q_rope.dtype, 4, host_ok=True)
+    _check(v, "v", q_rope.dtype, 4, host_ok=True)
+    _check(out, "out", q_rope.dtype, 3)
+    _check(tok_idx, "tok_idx", torch.int32, 3)
+    _check(tok_cnt, "tok_cnt", torch.int32, 2)
+    _check(lse, "lse", torch.float32)
+    B, Hq, d = q_rope.shape
+    Hkv, Lmax = v.shape[1], v.shape[2]
+    n_dom = 0 if dom_pairs is None else dom_pairs.shape[1]
+    _call("sa_sparse_attn_decode_static", _ptr(q_rope), _ptr(k), _ptr(k_rest), _ptr(v),
+          _dtype_code(q_rope), B, Hq, Hkv, Lmax, d, _ptr(cache_len), _ptr(dom_pairs), n_dom,
+          int(bool(slab)), _ptr(tok_idx), _ptr(tok_cnt), tok_idx.shape[-1], float(sm_scale),
+          _ptr(out), _ptr(lse), _stream(stream))
     return out
 
 

@@ -216,28 +216,58 @@ sa_status sa_sparse_attn_prefill(const void* q_rope, const void* k_rope, const v
                                      as_stream(stream)));
 }
 
-sa_status sa_sparse_attn_decode(const void* q_rope, const void* k, const void* k_rest,
-                                const void* v, sa_dtype dtype, int B, int Hq, int Hkv, int Lmax,
-                                int d, const int32_t* cache_len, const int32_t* dom_pairs,
-                                int n_dom, int slab, const int32_t* tok_idx,
-                                const int32_t* tok_cnt, int max_k, float sm_scale, void* out,
-                                float* lse, void* ws, size_t ws_bytes, void* stream) {
+// checks shared by both decode entry points
+static sa_status decode_args(const void* q_rope, const void* k, const void*& k_rest, const void*& v,
+                             sa_dtype dtype, int B, int Hq, int Hkv, int Lmax, int d,
+                             const int32_t* dom_pairs, int n_dom, int slab, const int32_t* tok_idx,
+                             const int32_t* tok_cnt, int max_k, const void* out) {
   if (!dtype_ok(dtype)) return SA_ERR_DTYPE;
   if (!q_rope || !k || !v || !tok_idx || !tok_cnt || !out) return SA_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Lmax < 1 || !head_dim_ok(d)) return SA_ERR_SHAPE;
   if (max_k < 1) return SA_ERR_RANGE;
+  if (static_cast<int64_t>(B) * Hq > 0x7fffffffLL) return SA_ERR_SHAPE;
   if (slab) {
     if (!dom_pairs) return SA_ERR_NULL;
     if (n_dom < 1 || 2 * n_dom > d) return SA_ERR_RANGE;
     if (n_dom % 4 != 0) return SA_ERR_UNSUPPORTED;
     if (2 * n_dom < d && !k_rest) return SA_ERR_NULL;
   }
+  return SA_OK;
+}
+
+sa_status sa_sparse_attn_decode(const void* q_rope, const void* k, const void* k_rest,
+                                const void* v, sa_dtype dtype, int B, int Hq, int Hkv, int Lmax,
+                                int d, const int32_t* cache_len, const int32_t* dom_pairs,
+                                int n_dom, int slab, const int32_t* tok_idx,
+                                const int32_t* tok_cnt, int max_k, float sm_scale, void* out,
+                                float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const sa_status a = decode_args(q_rope, k, k_rest, v, dtype, B, Hq, Hkv, Lmax, d, dom_pairs,
+                                  n_dom, slab, tok_idx, tok_cnt, max_k, out);
+  if (a != SA_OK) return a;
   const size_t need = sa::decode_ws_bytes(B, Hq, max_k);
   if (!ws || ws_bytes < need) return SA_ERR_WORKSPACE;
   if (!device_view(k_rest, &k_rest) || !device_view(v, &v)) return SA_ERR_ACCESS;
   return launched(sa::launch_decode(q_rope, k, k_rest, v, dtype, B, Hq, Hkv, Lmax, d, cache_len,
                                     dom_pairs, n_dom, slab ? 1 : 0, tok_idx, tok_cnt, max_k,
                                     sm_scale, out, lse, ws, as_stream(stream)));
+}
+
+sa_status sa_sparse_attn_decode_static(const void* q_rope, const void* k, const void* k_rest,
+                                       const void* v, sa_dtype dtype, int B, int Hq, int Hkv,
+                                       int Lmax, int d, const int32_t* cache_len,
+                                       const int32_t* dom_pairs, int n_dom, int slab,
+                                       const int32_t* tok_idx, const int32_t* tok_cnt, int max_k,
+                                       float sm_scale, void* out, float* lse, void* stream) {
+  const sa_status a = decode_args(q_rope, k, k_rest, v, dtype, B, Hq, Hkv, Lmax, d, dom_pairs,
+                                  n_dom, slab, tok_idx, tok_cnt, max_k, out);
+  if (a != SA_OK) return a;
+  if (sa::decode_scratch_bytes(B, Hq, max_k) > sa::kDecodeScratchBytes) return SA_ERR_WORKSPACE;
+  if (!device_view(k_rest, &k_rest) || !device_view(v, &v)) return SA_ERR_ACCESS;
+  void* scratch = nullptr;
+  if (sa::decode_static_scratch(&scratch) != hipSuccess) return SA_ERR_HIP;
+  return launched(sa::launch_decode(q_rope, k, k_rest, v, dtype, B, Hq, Hkv, Lmax, d, cache_len,
+                                    dom_pairs, n_dom, slab ? 1 : 0, tok_idx, tok_cnt, max_k,
+                                    sm_scale, out, lse, scratch, as_stream(stream)));
 }
 
 static bool calib_sizes_ok(int Hq, int Hkv, int M, int L, int d) {

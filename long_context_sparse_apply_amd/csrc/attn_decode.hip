@@ -23,13 +23,14 @@
 // k_dom part (read by the first 2*n_dom/8 lanes) and its k_rest part (the
 // other lanes); the query is permuted to the same channel order, since the
 // dot product does not depend on the order of channels.
+#include <mutex>
+
 #include "sa_common.hpp"
 
 namespace sa {
 
 // (chunk and wave counts: sa_limits.hpp; splits and workspace size: host_sizes.cpp)
 constexpr int kDecPerWave = kDecChunk / kDecWaves;
-constexpr int kChipCUs = 256;  // MI355X compute units
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
@@ -239,19 +240,39 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   if (lse && t == 0) lse[bh] = (L > 0.f) ? M + logf(L) : -INFINITY;
 }
 
+// Split-K partials of the allocation-free entry point: one array per GPU,
+// held until the process ends, located once per device with
+// hipGetSymbolAddress (in host code the array's name is not its device
+// address).  Calls that overlap on one GPU share it and race.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_decode(const void* q, const void* k, const void* k_rest, const void* v,
                          int dtype, int B, int Hq, int Hkv, int Lmax, int d,
                          const int32_t* cache_len, const int32_t* dom, int n_dom, int slab,
                          const int32_t* tok_idx, const int32_t* tok_cnt, int max_k, float scale,
                          void* out, float* lse, void* ws, hipStream_t st) {
   (void)cache_len;
-  // With at least two (b, h) rows per CU of the chip a work-group takes a
-  // whole selection list (one pass, no merge); otherwise each takes 256
-  // entries and a merge pass combines the splits.
-  const int nchunks = decode_splits(max_k);
-  const int rows = B * Hq;
-  const int cpw = rows >= 2 * kChipCUs ? nchunks : 1;
-  const int splits = (nchunks + cpw - 1) / cpw;
+  const DecodePlan plan = decode_plan(B, Hq, max_k);
+  const int cpw = plan.cpw;
+  const int splits = plan.splits;
   const int64_t parts = static_cast<int64_t>(B) * Hq * splits;
   float* ws_m = static_cast<float*>(ws);
   float* ws_l = ws_m + parts;

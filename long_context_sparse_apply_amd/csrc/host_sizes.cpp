@@ -33,6 +33,19 @@ size_t decode_ws_bytes(int B, int Hq, int max_k) {
   return parts * (2 + 128) * sizeof(float) + 256;
 }
 
+DecodePlan decode_plan(int B, int Hq, int max_k) {
+  const int nchunks = decode_splits(max_k);
+  const int64_t rows = static_cast<int64_t>(B) * Hq;
+  const int cpw = rows >= 2 * kChipCUs ? nchunks : 1;
+  return DecodePlan{(nchunks + cpw - 1) / cpw, cpw};
+}
+
+size_t decode_scratch_bytes(int B, int Hq, int max_k) {
+  const DecodePlan p = decode_plan(B, Hq, max_k);
+  if (p.splits <= 1) return 0;
+  return static_cast<size_t>(B) * Hq * p.splits * (2 + 128) * sizeof(float);
+}
+
 // LDS of one long-row top-k work-group: candidate composites, the radix
 // histogram, the row's bitmap and per-wave scratch
 size_t topk_lds_bytes(int cols, int cap) {

@@ -74,9 +74,23 @@ hipError_t launch_token_score(const void* q, const void* k, int dtype, int B, in
                               int Lmax, int d, const int32_t* cache_len, const int32_t* dom,
                               int n_dom, int slab, float scale, float* scores, hipStream_t st);
 
-// decode: split-K partials in ws, then the merge
+// decode: split-K partials in ws, then the merge.  With at least two (b, h)
+// lists per CU of the chip a work-group takes a whole list (cpw = all its
+// chunks, one pass, no partials); otherwise each takes one chunk and a merge
+// pass combines the splits.
 int decode_splits(int max_k);
 size_t decode_ws_bytes(int B, int Hq, int max_k);
+struct DecodePlan {
+  int splits;  // work-groups per (b, h) list
+  int cpw;     // 256-token chunks per work-group
+};
+DecodePlan decode_plan(int B, int Hq, int max_k);
+// partials the launch actually writes (0 for the one-pass form)
+size_t decode_scratch_bytes(int B, int Hq, int max_k);
+// the allocation-free decode entry point's per-device array
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t decode_static_scratch(void** ptr);
 hipError_t launch_decode(const void* q, const void* k, const void* k_rest, const void* v,
                          int dtype, int B, int Hq, int Hkv, int Lmax, int d,
                          const int32_t* cache_len, const int32_t* dom, int n_dom, int slab,

@@ -10,6 +10,7 @@ constexpr int kWave = 64;  // wavefront width on gfx950
 // split-K decode attention: tokens per work-group chunk, waves per work-group
 constexpr int kDecChunk = 256;
 constexpr int kDecWaves = 4;
+constexpr int kChipCUs = 256;  // MI355X compute units
 
 // long-row top-k: threads per row, radix digit, largest LDS candidate
 // buffer (64-bit composites), longest row the host accepts

@@ -130,6 +130,15 @@ int main() {
     expect(SA_ERR_UNSUPPORTED, nullptr, [&] { return sa_sparse_attn_decode(dev(), dev(), dev(), dev(), BF, 2, 8, 2, 3000, 128, nullptr, idev(), 6, 1, idev(), idev(), 700, 0.088f, dev(), nullptr, dev(), need, nullptr); });
   }
 
+  // ---- the allocation-free decode: partials in the library's array
+  expect(SA_OK, "decode", [&] { return sa_sparse_attn_decode_static(dev(), dev(), nullptr, dev(0x20), BF, 2, 8, 2, 3000, 128, nullptr, nullptr, 0, 0, idev(), idev(), 700, 0.088f, dev(), nullptr, nullptr); });
+  // one-pass form (B * Hq >= 512) needs no partials, whatever max_k
+  expect(SA_OK, "decode", [&] { return sa_sparse_attn_decode_static(dev(), dev(), nullptr, dev(), BF, 64, 32, 8, 131072, 128, nullptr, nullptr, 0, 0, idev(), idev(), 131072, 0.088f, dev(), nullptr, nullptr); });
+  // 511 lists x 64 splits x 520 B > 16 MiB
+  expect(SA_ERR_WORKSPACE, nullptr, [&] { return sa_sparse_attn_decode_static(dev(), dev(), nullptr, dev(), BF, 1, 511, 511, 20000, 128, nullptr, nullptr, 0, 0, idev(), idev(), 16384, 0.088f, dev(), nullptr, nullptr); });
+  expect(SA_ERR_ACCESS, nullptr, [&] { return sa_sparse_attn_decode_static(dev(), dev(), nullptr, pageable(), BF, 2, 8, 2, 3000, 128, nullptr, nullptr, 0, 0, idev(), idev(), 700, 0.088f, dev(), nullptr, nullptr); });
+  expect(SA_ERR_NULL, nullptr, [&] { return sa_sparse_attn_decode_static(dev(), dev(), nullptr, dev(), BF, 2, 8, 2, 3000, 128, nullptr, nullptr, 0, 0, nullptr, idev(), 700, 0.088f, dev(), nullptr, nullptr); });
+
   // ---- calibration, feature codes
   {
     const size_t need = sa_calibrate_workspace_bytes(32, 8, 16, 8192, 128, 256);

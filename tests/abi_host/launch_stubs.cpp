@@ -107,4 +107,9 @@ hipError_t launch_calibrate(const void* q, const void*, int, int, int, int, int,
   return hit("calibrate", q, ws);
 }
 
+hipError_t decode_static_scratch(void** ptr) {
+  *ptr = reinterpret_cast<void*>(kDevLo + 0x800000);
+  return hipSuccess;
+}
+
 }  // namespace sa
