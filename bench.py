@@ -359,8 +359,13 @@ def run_decode(cfg, steps, warmup, torch, flush):
     from long_context_sparse_apply_amd.pipeline import DecodeStep
     dt = SD.decode_tensors(cfg)
     step = DecodeStep(dt["q_raw"], dt["k"], dt["v"], dt["lens"], dt["dom"], theta=cfg.theta,
-                      top_k=cfg.k, slab=bool(cfg.slab), k_rest=dt["k_rest"])
+                      top_k=cfg.k, slab=bool(cfg.slab), k_rest=dt["k_rest"], k_full=dt["k_full"])
     t = time_decode(step, steps, warmup, torch, flush)
+    t["cache_layout"] = ("standard" if not cfg.slab else
+                         "dominant slab + full rows" if cfg.full_rows else "dominant slab + rest")
+    t["cache_device_bytes"] = float(sum(x.numel() * x.element_size()
+                                        for x in (dt["k"], dt["k_rest"], dt["k_full"], dt["v"])
+                                        if x is not None))
     cnt = step.tok_cnt.cpu().numpy()
     gb = decode_bytes(cnt, cfg.d)
     t["attend_gather_bytes"] = gb
@@ -376,7 +381,8 @@ def run_decode(cfg, steps, warmup, torch, flush):
         t["score_hbm_frac"] = key_bytes / (t["score_select_us"] * 1e-6) / PEAK_HBM_BPS
         # the two calls it replaces, on the same inputs, for comparison
         two = DecodeStep(dt["q_raw"], dt["k"], dt["v"], dt["lens"], dt["dom"], theta=cfg.theta,
-                         top_k=cfg.k, slab=bool(cfg.slab), k_rest=dt["k_rest"], fused=False)
+                         top_k=cfg.k, slab=bool(cfg.slab), k_rest=dt["k_rest"], k_full=dt["k_full"],
+                         fused=False)
         two.rope()
 
         def score_then_select():
@@ -397,24 +403,17 @@ def run_decode(cfg, steps, warmup, torch, flush):
     return t
 
 
-def cpu_baseline(cfg):
-    """The fp64 oracle on the whole 32K prefill layer (every query head): block
-    scoring, selection and block-sparse attention, timed on the host cores."""
-    from oracle import sparse_attention as O
-    from synth import workloads as W
-    heads = list(range(cfg.Hq))
-    q, k, v, _ = W.prefill_inputs_host(cfg, q_heads=heads)
-    t0 = time.perf_counter()
-    O.prefill_pipeline(q, k, v, theta=cfg.theta, block=cfg.block,
-                       split_pair=cfg.band_split_pair, calibrate=True, sm_scale=cfg.d ** -0.5,
-                       causal=True, budget=O.keep_budget(cfg.N, keep_percent=cfg.keep_percent),
-                       n_sink=cfg.n_sink, n_local=cfg.n_local, q_heads=heads, group=cfg.group)
-    dt = time.perf_counter() - t0
+def host_info():
+    """Cores in this process's affinity mask, BLAS threads, CPU model."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        blas = 1
     cpu_model = "unknown CPU"
     try:
         for line in open("/proc/cpuinfo"):
@@ -423,10 +422,87 @@ def cpu_baseline(cfg):
                 break
     except OSError:  # pragma: no cover
         pass
-    return {"value": cfg.B * cfg.S / dt, "unit": "tok/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"the whole 32K prefill layer ({cfg.Hq} query heads, {cfg.S} tokens), "
-                      f"one pass: {dt:.1f} s on {cpu_model}"}
+    return affinity, blas, cpu_model
+
+
+def _spot_check(host, seed, tid, base, rng, n=4096):
+    """The copied inputs are the seeded generator's values: a random sample of
+    elements regenerated on the host must match bit for bit."""
+    import synth
+    flat = host.reshape(-1)
+    idx = rng.integers(0, flat.size, n)
+    want = synth.round_to_bf16(synth.gaussian_f32(seed, tid, (base + idx).astype(np.uint64)))
+    assert np.array_equal(flat[idx].astype(np.float32), want), "inputs differ from the generator"
+
+
+def _baseline(value, unit, seconds, sample):
+    affinity, blas, cpu_model = host_info()
+    return {"value": value, "unit": unit, "cores": int(blas), "kind": "oracle",
+            "sample": f"{sample}: {seconds:.1f} s on {cpu_model}",
+            "affinity_cores": int(affinity), "blas_threads": int(blas),
+            "python_threads": 1, "cpu_model": cpu_model}
+
+
+def cpu_baseline_prefill(cfg, torch, kv_groups=None):
+    """The fp64 oracle on a prefill layer: block scoring, selection and
+    block-sparse attention, timed on the host cores.  ``kv_groups`` limits it
+    to those KV groups (their query heads), extrapolated linearly in heads.
+    Inputs come from the device-side seeded generator (copied to the host and
+    spot-checked against the host generator); only the oracle is timed."""
+    import synth
+    import synth.device as SD
+    from oracle import sparse_attention as O
+    groups = list(range(cfg.Hkv)) if kv_groups is None else list(kv_groups)
+    heads = [g * cfg.group + i for g in groups for i in range(cfg.group)]
+    qd, kd, vd = SD.prefill_tensors(cfg)
+    q = qd[:, heads].float().cpu().numpy()
+    k = kd.float().cpu().numpy()
+    v = vd.float().cpu().numpy()
+    del qd, kd, vd
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(0)
+    _spot_check(v, cfg.seed, synth.TID_V, 0, rng)
+    t0 = time.perf_counter()
+    O.prefill_pipeline(q, k, v, theta=cfg.theta, block=cfg.block,
+                       split_pair=cfg.band_split_pair, calibrate=True, sm_scale=cfg.d ** -0.5,
+                       causal=True, budget=O.keep_budget(cfg.N, keep_percent=cfg.keep_percent),
+                       n_sink=cfg.n_sink, n_local=cfg.n_local, q_heads=heads, group=cfg.group)
+    dt = time.perf_counter() - t0
+    scale = cfg.Hq / len(heads)
+    what = (f"the whole {cfg.S // 1024}K prefill layer ({cfg.Hq} query heads), one pass"
+            if scale == 1 else
+            f"{len(groups)} KV group(s) ({len(heads)} of {cfg.Hq} query heads) of the "
+            f"{cfg.S // 1024}K prefill layer, extrapolated x{scale:g} (work is linear in heads)")
+    return _baseline(cfg.B * cfg.S / (dt * scale), "tok/s", dt, what)
+
+
+def cpu_baseline_decode(cfg, torch, batches):
+    """The fp64 oracle on a decode step (rotate q, token scores over the
+    dominant pairs, top-k, attention) for the sampled batch rows, extrapolated
+    linearly to the whole batch (work is linear in batch rows)."""
+    import synth
+    import synth.device as SD
+    from oracle import sparse_attention as O
+    dt_ = SD.decode_tensors(cfg)
+    bs = list(batches)
+    kfull = dt_["k_full"] if dt_.get("k_full") is not None else dt_["k"]
+    if cfg.slab and dt_.get("k_full") is None:
+        raise ValueError("the decode baseline reads full key rows")
+    q = dt_["q_raw"][bs].float().cpu().numpy()
+    k = kfull[bs].float().cpu().numpy()
+    v = dt_["v"][bs].float().cpu().numpy()
+    lens, dom = dt_["lens_host"][bs], dt_["dom_host"]
+    del dt_, kfull
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(1)
+    _spot_check(v[0], cfg.seed, synth.TID_V, bs[0] * cfg.Hkv * cfg.L * cfg.d, rng)
+    t0 = time.perf_counter()
+    O.decode_pipeline(q, k, v, lens, dom, theta=cfg.theta, k=cfg.k, sm_scale=cfg.d ** -0.5)
+    dt = time.perf_counter() - t0
+    scale = cfg.B / len(bs)
+    what = (f"batch rows {bs[0]}-{bs[-1]} of {cfg.B} ({len(bs) * cfg.Hq} of {cfg.B * cfg.Hq} "
+            f"query rows), KV length {cfg.L}, top-{cfg.k}, extrapolated x{scale:g}")
+    return _baseline(dt * scale * 1e6, "us/step", dt, what)
 
 
 def measured_traffic(summary_path, kernel_source):
@@ -502,7 +578,8 @@ def main():
                                      "attend_ms": r3["attend_ms"],
                                      "attend_mfma_frac": r3["attend_mfma_frac"],
                                      "score_ms": r3["score_ms"], "select_ms": r3["select_ms"]}
-        for name, c in (("decode_64k", W.C4), ("decode_128k_slab", W.C5)):
+        for name, c in (("decode_64k", W.C4), ("decode_128k_slab", W.C5),
+                        ("decode_128k_slab_rest", W.C5.with_(full_rows=0))):
             log(f"{name}")
             rd = run_decode(c, args.steps, args.warmup, torch, flush)
             log(json.dumps(rd))
@@ -516,12 +593,14 @@ def main():
                                "attend_gather_bytes": rd["attend_gather_bytes"],
                                "attend_gather_bytes_dedup_per_kv_head":
                                    rd["attend_gather_bytes_dedup_per_kv_head"],
-                               "score_hbm_frac": rd["score_hbm_frac"]}
+                               "score_hbm_frac": rd["score_hbm_frac"],
+                               "cache_layout": rd["cache_layout"],
+                               "cache_device_bytes": rd["cache_device_bytes"]}
             if rd["fused"]:
                 secondary[name]["two_step_score_select_us"] = rd["two_step_score_select_us"]
                 secondary[name]["two_step_equal"] = rd["two_step_equal"]
         log("decode_64k_slab_host_rest (FASA-M placement)")
-        cfg_m = W.C5.with_(B=16, L=65536, k=2048)
+        cfg_m = W.C5.with_(B=16, L=65536, k=2048, full_rows=0)
         rm = run_decode_host_rest(cfg_m, max(2, args.steps // 5), 1, torch, flush)
         log(json.dumps(rm))
         secondary["decode_64k_slab_host_rest"] = {
@@ -545,9 +624,20 @@ def main():
         log(json.dumps(ra))
         secondary["cache_append"] = ra
     cpu = None
+    cpu_more = None
     if not args.no_cpu:
-        log("cpu baseline (oracle)")
-        cpu = cpu_baseline(cfg)
+        log("cpu baseline (oracle): 32K prefill layer")
+        cpu = cpu_baseline_prefill(cfg, torch)
+        log(json.dumps(cpu))
+        if not args.no_secondary:
+            cpu_more = {}
+            log("cpu baseline (oracle): 128K prefill, one KV group")
+            cpu_more["prefill_128k"] = cpu_baseline_prefill(W.C3, torch, kv_groups=[0])
+            log("cpu baseline (oracle): 64K decode, batch rows 0-1")
+            cpu_more["decode_64k"] = cpu_baseline_decode(W.C4, torch, [0, 1])
+            log("cpu baseline (oracle): 128K slab decode, batch rows 0-3")
+            cpu_more["decode_128k_slab"] = cpu_baseline_decode(W.C5, torch, [0, 1, 2, 3])
+            log(json.dumps(cpu_more))
     # the roofline uses the attention kernel's mean launch duration (as a
     # kernel trace reports it); the step figures are medians
     achieved = main_r["attend_flops"] / (main_r["attend_ms_mean"] * 1e-3) / 1e12
@@ -583,6 +673,7 @@ def main():
                    "HIP events on the kernels' stream; medians of the timed steps; no cache flush"),
         "hbm_reference": {"copy_GBps": copy_gbps, "peak_GBps": PEAK_HBM_BPS / 1e9},
         "cpu_baseline": cpu,
+        "cpu_baseline_secondary": cpu_more,
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)

@@ -93,6 +93,13 @@ sa_status sa_rope_apply(const void* x, void* out, sa_dtype dtype, int B, int H, 
  *   slab == 1: k_cache = k_dom [B, Hkv, Lmax, 2*n_dom] and k_rest
  *           [B, Hkv, Lmax, d - 2*n_dom], laid out as in sa_token_score
  *           (dom_pairs [Hkv, n_dom], distinct pairs < d/2).
+ *   slab == 2 (slab + full rows): k_cache = k_dom as for slab == 1, and
+ *           k_rest = the full rotated rows [B, Hkv, Lmax, d] in the standard
+ *           layout.  Scoring reads the slab; the attention gathers whole
+ *           rows of k_rest (sa_sparse_attn_decode with slab == 0), each
+ *           256-byte row two whole cache lines instead of a 64-byte slab
+ *           piece plus a 192-byte rest piece straddling three, for 2*n_dom
+ *           channels of extra memory per token.
  *   v_cache [B, Hkv, Lmax, d].  k_rest and v_cache may be pinned host memory
  *           (host placement, FASA-M).
  * The angle p * omega_i is formed and reduced modulo 2*pi in fp64, the
@@ -101,8 +108,9 @@ sa_status sa_rope_apply(const void* x, void* out, sa_dtype dtype, int B, int H, 
  * on the host; out-of-range values give undefined cache contents, never a
  * write outside the cache.
  * Errors: SA_ERR_NULL, SA_ERR_SHAPE (B, Hkv, S, Lmax < 1 or d not 64/128),
- *         SA_ERR_RANGE (theta <= 1, n_dom outside [1, d/2]), SA_ERR_DTYPE,
- *         SA_ERR_ACCESS (k_rest or v_cache in pageable host memory).
+ *         SA_ERR_RANGE (theta <= 1, slab not 0/1/2, n_dom outside [1, d/2]),
+ *         SA_ERR_DTYPE, SA_ERR_ACCESS (k_rest or v_cache in pageable host
+ *         memory).
  */
 sa_status sa_kv_cache_append(const void* k_new, const void* v_new, sa_dtype dtype, int B,
                              int Hkv, int S, int d, int Lmax, const int32_t* start, double theta,

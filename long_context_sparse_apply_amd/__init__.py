@@ -145,14 +145,17 @@ def sa_rope_apply(x, out, theta: float, pos=None, pos0: int = 0, stream=None):
 
 
 def sa_kv_cache_append(k_new, v_new, start, k_cache, v_cache, *, theta: float, k_rest=None,
-                       dom_pairs=None, slab: bool = False, stream=None):
+                       dom_pairs=None, slab: bool = False, full_rows: bool = False,
+                       stream=None):
     """Write new tokens into a decode KV cache.
 
     k_new, v_new: [B, Hkv, S, d] raw keys and values; start: int32 [B], the
     cache row (= absolute position) of each batch's first new token.
     slab False: k_cache [B, Hkv, Lmax, d].  slab True: k_cache = k_dom
     [B, Hkv, Lmax, 2*n_dom], k_rest [B, Hkv, Lmax, d - 2*n_dom], dom_pairs
-    int32 [Hkv, n_dom].  v_cache [B, Hkv, Lmax, d].
+    int32 [Hkv, n_dom]; with full_rows, k_rest holds the full rotated rows
+    [B, Hkv, Lmax, d] instead (the slab + full-row layout).  v_cache
+    [B, Hkv, Lmax, d].
     """
     torch = _torch()
     _check(k_new, "k_new", ndim=4)
@@ -175,12 +178,16 @@ def sa_kv_cache_append(k_new, v_new, start, k_cache, v_cache, *, theta: float, k
         n_dom = dom_pairs.shape[1]
         if tuple(k_cache.shape) != (B, Hkv, Lmax, 2 * n_dom):
             raise ValueError("k_dom must be [B, Hkv, Lmax, 2*n_dom]")
-        if k_rest is not None and tuple(k_rest.shape) != (B, Hkv, Lmax, d - 2 * n_dom):
-            raise ValueError("k_rest must be [B, Hkv, Lmax, d - 2*n_dom]")
+        rest_w = d if full_rows else d - 2 * n_dom
+        if k_rest is not None and tuple(k_rest.shape) != (B, Hkv, Lmax, rest_w):
+            raise ValueError(f"k_rest must be [B, Hkv, Lmax, {rest_w}]")
+    elif full_rows:
+        raise ValueError("full_rows needs the slab layout")
     elif tuple(k_cache.shape) != (B, Hkv, Lmax, d):
         raise ValueError("k_cache must be [B, Hkv, Lmax, d]")
+    layout = 0 if not slab else (2 if full_rows else 1)
     _call("sa_kv_cache_append", _ptr(k_new), _ptr(v_new), _dtype_code(k_new), B, Hkv, S, d, Lmax,
-          _ptr(start), float(theta), int(bool(slab)), _ptr(dom_pairs), n_dom, _ptr(k_cache),
+          _ptr(start), float(theta), layout, _ptr(dom_pairs), n_dom, _ptr(k_cache),
           _ptr(k_rest), _ptr(v_cache), _stream(stream))
 
 

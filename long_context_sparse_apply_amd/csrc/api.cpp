@@ -65,18 +65,18 @@ sa_status sa_kv_cache_append(const void* k_new, const void* v_new, sa_dtype dtyp
   if (!dtype_ok(dtype)) return SA_ERR_DTYPE;
   if (!k_new || !v_new || !start || !k_cache || !v_cache) return SA_ERR_NULL;
   if (B < 1 || Hkv < 1 || S < 1 || Lmax < 1 || !head_dim_ok(d)) return SA_ERR_SHAPE;
-  if (!(theta > 1.0)) return SA_ERR_RANGE;
+  if (!(theta > 1.0) || slab < 0 || slab > 2) return SA_ERR_RANGE;
   if (slab) {
     if (!dom_pairs) return SA_ERR_NULL;
     if (n_dom < 1 || 2 * n_dom > d) return SA_ERR_RANGE;
-    if (2 * n_dom < d && !k_rest) return SA_ERR_NULL;
+    if ((slab == 2 || 2 * n_dom < d) && !k_rest) return SA_ERR_NULL;
   }
   const void* kr = nullptr;
   const void* vc = nullptr;
   if (!device_view(k_rest, &kr) || !device_view(v_cache, &vc)) return SA_ERR_ACCESS;
   const sa::RopeFreq fr = sa::make_rope_freq(d, theta);
   return launched(sa::launch_kv_append(k_new, v_new, dtype, B, Hkv, S, d, Lmax, start, fr,
-                                       slab ? 1 : 0, dom_pairs, slab ? n_dom : 0, k_cache,
+                                       slab, dom_pairs, slab ? n_dom : 0, k_cache,
                                        const_cast<void*>(kr), const_cast<void*>(vc),
                                        as_stream(stream)));
 }

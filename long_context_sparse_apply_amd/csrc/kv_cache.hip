@@ -1,5 +1,6 @@
 // Appending tokens to a decode KV cache: keys rotated at their absolute
-// positions, in the standard or the dominant-slab layout, plus values.
+// positions, in the standard layout, the dominant-slab layout (slab + rest)
+// or the slab plus full rows, plus values.
 //
 // "FASA: Frequency-aware Sparse Attention", sec. 2.B item 2 (attention over
 // the selected tokens keeps their original absolute positions, so the cache
@@ -16,7 +17,10 @@
 // work-group's part of each slab is one contiguous run, written with
 // coalesced stores that gather channels through a slot -> channel table:
 // slot j < n_dom holds D[j], slot n_dom + j holds D[j] + P, and the rest slab
-// holds every other channel in ascending order.  Values are copied unrotated.
+// holds every other channel in ascending order.  With slab + full rows
+// (layout 2) the whole rotated row also goes, in the standard channel order,
+// to the full-row cache, which the attention gathers as aligned 256-byte rows.
+// Values are copied unrotated.
 #include "sa_common.hpp"
 
 namespace sa {
@@ -96,10 +100,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
       ra[j] = a[j] * cs - bb[j] * sn;
       rb[j] = bb[j] * cs + a[j] * sn;
     }
-    if (!slab) {
-      Elem<T>::store8(k_out + dst * D + 8 * c, ra);
-      Elem<T>::store8(k_out + dst * D + P + 8 * c, rb);
-    } else {
+    if (slab != 1) {
+      T* full = slab == 0 ? k_out : k_rest;  // layout 2: k_rest holds the full rows
+      Elem<T>::store8(full + dst * D + 8 * c, ra);
+      Elem<T>::store8(full + dst * D + P + 8 * c, rb);
+    }
+    if (slab) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         s_rows[rl][8 * c + j] = ra[j];
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     }
   };
   write_run(k_out + row0 * ndc, ndc, 0);
-  if (nrest > 0) write_run(k_rest + row0 * nrest, nrest, ndc);
+  if (slab == 1 && nrest > 0) write_run(k_rest + row0 * nrest, nrest, ndc);
 }
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, int dtype, int B, int Hkv,

@@ -140,9 +140,12 @@ class DecodeCache:
 
     Keys are stored rotated at their absolute positions (the row index), in
     the standard layout ``k [B, Hkv, Lmax, d]`` or, with ``slab``, as the
-    dominant slab ``k [B, Hkv, Lmax, 2*n_dom]`` plus ``k_rest [B, Hkv, Lmax,
-    d - 2*n_dom]``.  ``lens`` (int32 [B], on the device) counts the rows
-    written so far; appends go to row ``lens[b]`` onward.
+    dominant slab ``k [B, Hkv, Lmax, 2*n_dom]`` plus either ``k_rest [B, Hkv,
+    Lmax, d - 2*n_dom]`` or, with ``full_rows``, ``k_full [B, Hkv, Lmax, d]``
+    (every channel in the standard order: the attention then gathers whole
+    256-byte rows, for 2*n_dom channels of extra memory per token).  ``lens``
+    (int32 [B], on the device) counts the rows written so far; appends go to
+    row ``lens[b]`` onward.
 
     ``host_rest`` (slab layout only): FASA's memory-optimised variant
     (FASA-M, sec. 2.C).  Only the dominant slab stays in device memory;
@@ -151,17 +154,21 @@ class DecodeCache:
     """
 
     def __init__(self, B, Hkv, Lmax, d, *, dtype, device, theta, dom_pairs, slab=False,
-                 host_rest=False):
+                 full_rows=False, host_rest=False):
         if host_rest and not slab:
             raise ValueError("host placement keeps the dominant slab on the device: needs slab")
+        if full_rows and (not slab or host_rest):
+            raise ValueError("full rows go with the device-resident slab layout")
         self.B, self.Hkv, self.Lmax, self.d = B, Hkv, Lmax, d
-        self.theta, self.slab, self.dom = theta, slab, dom_pairs
+        self.theta, self.slab, self.full_rows, self.dom = theta, slab, full_rows, dom_pairs
         n_dom = dom_pairs.shape[1]
         kd = 2 * n_dom if slab else d
         rest_kw = dict(device="cpu", pin_memory=True) if host_rest else dict(device=device)
         self.k = torch.zeros((B, Hkv, Lmax, kd), dtype=dtype, device=device)
         self.k_rest = (torch.zeros((B, Hkv, Lmax, d - kd), dtype=dtype, **rest_kw)
-                       if slab and kd < d else None)
+                       if slab and not full_rows and kd < d else None)
+        self.k_full = (torch.zeros((B, Hkv, Lmax, d), dtype=dtype, device=device)
+                       if full_rows else None)
         self.v = torch.zeros((B, Hkv, Lmax, d), dtype=dtype, **rest_kw)
         self.lens = torch.zeros(B, dtype=torch.int32, device=device)
 
@@ -171,27 +178,31 @@ class DecodeCache:
         are dropped and not counted."""
         S = k_new.shape[2]
         sl = slice(None) if batch is None else slice(batch, batch + 1)
-        k_rest = None if self.k_rest is None else self.k_rest[sl]
+        second = self.k_full if self.full_rows else self.k_rest
         lens = self.lens[sl]
         sa_kv_cache_append(k_new, v_new, lens, self.k[sl], self.v[sl], theta=self.theta,
-                           k_rest=k_rest, dom_pairs=self.dom, slab=self.slab)
+                           k_rest=None if second is None else second[sl], dom_pairs=self.dom,
+                           slab=self.slab, full_rows=self.full_rows)
         lens.add_(S).clamp_(max=self.Lmax)
 
     def step(self, q_raw, *, top_k, sm_scale=None):
         """A decode step for the query ``q_raw [B, Hq, d]`` of the newest token."""
         return DecodeStep(q_raw, self.k, self.v, self.lens, self.dom, theta=self.theta,
-                          top_k=top_k, slab=self.slab, k_rest=self.k_rest, sm_scale=sm_scale)
+                          top_k=top_k, slab=self.slab, k_rest=self.k_rest, k_full=self.k_full,
+                          sm_scale=sm_scale)
 
 
 class DecodeStep:
     """One decode step.  ``fused`` (the default for the slab layout, and for
     the standard layout in bf16 with at most 16 dominant pairs) scores and
     selects the tokens with sa_token_topk, which writes no score array;
-    otherwise sa_token_score then sa_topk_select (the same selection)."""
+    otherwise sa_token_score then sa_topk_select (the same selection).
+    ``k_full`` (slab layout): the full rotated rows the attention gathers,
+    in place of the slab and ``k_rest``."""
 
     def __init__(self, q_raw, k, v, cache_len, dom_pairs, *, theta, top_k, slab=False, k_rest=None,
-                 sm_scale=None, cache_len_host=None, fused=None):
-        self.q_raw, self.k, self.v, self.k_rest = q_raw, k, v, k_rest
+                 k_full=None, sm_scale=None, cache_len_host=None, fused=None):
+        self.q_raw, self.k, self.v, self.k_rest, self.k_full = q_raw, k, v, k_rest, k_full
         B, Hq, d = q_raw.shape
         Hkv, L = v.shape[1], v.shape[2]
         self.B, self.Hq, self.Hkv, self.L, self.d = B, Hq, Hkv, L, d
@@ -240,6 +251,12 @@ class DecodeStep:
                       self.ws_sel, sm_scale=self.scale, k_top=self.top_k, slab=self.slab)
 
     def attend(self):
+        if self.k_full is not None:
+            # slab + full rows: the attention gathers whole rows of the full cache
+            sa_sparse_attn_decode(self.q_rope, self.k_full, self.v, self.tok_idx, self.tok_cnt,
+                                  self.out, self.ws, sm_scale=self.scale,
+                                  cache_len=self.cache_len, lse=self.lse)
+            return
         sa_sparse_attn_decode(self.q_rope, self.k, self.v, self.tok_idx, self.tok_cnt, self.out,
                               self.ws, sm_scale=self.scale, cache_len=self.cache_len,
                               dom_pairs=self.dom, slab=self.slab, k_rest=self.k_rest,

@@ -111,23 +111,31 @@ def decode_tensors(cfg: W.DecodeConfig, device="cuda"):
             k[b, h // cfg.group, p] = torch.from_numpy(row).to(device=device, dtype=dt)
         out["k"] = k
         out["k_rest"] = None
+        out["k_full"] = None
     else:
         maps = [W.slab_channels(dom[g], cfg.d) for g in range(cfg.Hkv)]
         dom_map = torch.from_numpy(np.stack([m[0] for m in maps]).astype(np.int32)).to(device)
         rest_map = torch.from_numpy(np.stack([m[1] for m in maps]).astype(np.int32)).to(device)
         nd = 2 * cfg.n_dom
         k_dom = torch.empty((cfg.B, cfg.Hkv, cfg.L, nd), dtype=dt, device=device)
-        k_rest = torch.empty((cfg.B, cfg.Hkv, cfg.L, cfg.d - nd), dtype=dt, device=device)
         fill(k_dom, cfg.seed, TID_K, logical_d=cfg.d, chmap=dom_map, rows_per_head=cfg.L,
              n_heads=cfg.Hkv)
-        fill(k_rest, cfg.seed, TID_K, logical_d=cfg.d, chmap=rest_map, rows_per_head=cfg.L,
-             n_heads=cfg.Hkv)
+        if cfg.full_rows:
+            # the full rows the attention gathers, in the standard channel order
+            k_second = torch.empty((cfg.B, cfg.Hkv, cfg.L, cfg.d), dtype=dt, device=device)
+            fill(k_second, cfg.seed, TID_K)
+        else:
+            k_second = torch.empty((cfg.B, cfg.Hkv, cfg.L, cfg.d - nd), dtype=dt, device=device)
+            fill(k_second, cfg.seed, TID_K, logical_d=cfg.d, chmap=rest_map, rows_per_head=cfg.L,
+                 n_heads=cfg.Hkv)
         for b, h, p, row in patches:
             g = h // cfg.group
             dm, rm = maps[g]
             k_dom[b, g, p] = torch.from_numpy(row[dm]).to(device=device, dtype=dt)
-            k_rest[b, g, p] = torch.from_numpy(row[rm]).to(device=device, dtype=dt)
+            k_second[b, g, p] = torch.from_numpy(row if cfg.full_rows else row[rm]).to(
+                device=device, dtype=dt)
         out["k"] = k_dom
-        out["k_rest"] = k_rest
+        out["k_rest"] = None if cfg.full_rows else k_second
+        out["k_full"] = k_second if cfg.full_rows else None
     torch.cuda.synchronize()
     return out

@@ -85,6 +85,7 @@ class DecodeConfig:
     needles_per_head: int = 4
     seed: int = 4
     ragged: int = 0           # if > 0, cache lengths vary in [L - ragged, L]
+    full_rows: int = 0        # slab layout: full rotated rows for the attention, not a rest slab
 
     @property
     def group(self) -> int:
@@ -103,8 +104,9 @@ C3 = PrefillConfig("Llama-3.1-8B-shaped prefill layer, seq 131072, bf16", "bf16"
                    needle_pairs=64, seed=3)
 C4 = DecodeConfig("token-sparse decode, batch 16, KV length 65536, bf16", "bf16", 16, 32, 8,
                   65536, 128, 5e5, n_dom=16, k=2048, slab=0, seed=4)
-C5 = DecodeConfig("token-sparse decode, batch 64, KV length 131072, dominant slab, bf16", "bf16",
-                  64, 32, 8, 131072, 128, 5e5, n_dom=16, k=4096, slab=1, seed=5)
+C5 = DecodeConfig("token-sparse decode, batch 64, KV length 131072, dominant slab + full rows, bf16",
+                  "bf16", 64, 32, 8, 131072, 128, 5e5, n_dom=16, k=4096, slab=1, seed=5,
+                  full_rows=1)
 
 CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
 

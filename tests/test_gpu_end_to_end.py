@@ -115,7 +115,7 @@ def _decode_step(sa, cfg, x, dt_inputs):
     from long_context_sparse_apply_amd.pipeline import DecodeStep
     return DecodeStep(dt_inputs["q_raw"], dt_inputs["k"], dt_inputs["v"], dt_inputs["lens"],
                       dt_inputs["dom"], theta=cfg.theta, top_k=cfg.k, slab=bool(cfg.slab),
-                      k_rest=dt_inputs.get("k_rest"))
+                      k_rest=dt_inputs.get("k_rest"), k_full=dt_inputs.get("k_full"))
 
 
 class _HostCache:
@@ -245,8 +245,9 @@ def _all_samples(cfg, batches):
 
 @pytest.mark.parametrize("name,cfg", [
     ("std-16k", W.C4.with_(B=2, L=16384, k=512, ragged=3000)),
-    ("slab-8k", W.C5.with_(B=2, L=8192, k=256, ragged=1000)),
-], ids=["std-16k", "slab-8k"])
+    ("slab-full-rows-8k", W.C5.with_(B=2, L=8192, k=256, ragged=1000)),
+    ("slab-rest-8k", W.C5.with_(B=2, L=8192, k=256, ragged=1000, full_rows=0)),
+], ids=["std-16k", "slab-full-rows-8k", "slab-rest-8k"])
 def test_decode_end_to_end(sa, name, cfg):
     import synth.device as SD
     say(f"case: decode end-to-end {name}")
@@ -312,7 +313,7 @@ def DecodeStepFor(cfg, dt_inputs):
     from long_context_sparse_apply_amd.pipeline import DecodeStep
     return DecodeStep(dt_inputs["q_raw"], dt_inputs["k"], dt_inputs["v"], dt_inputs["lens"],
                       dt_inputs["dom"], theta=cfg.theta, top_k=cfg.k, slab=bool(cfg.slab),
-                      k_rest=dt_inputs.get("k_rest"))
+                      k_rest=dt_inputs.get("k_rest"), k_full=dt_inputs.get("k_full"))
 
 
 @pytest.mark.parametrize("slab", [0, 1], ids=["std", "slab"])

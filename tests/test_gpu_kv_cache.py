@@ -88,7 +88,18 @@ def _check_cache(cache_k, cache_rest, cache_v, hc, dtype, dom, slab):
         other = np.nonzero(~w[b])[0]
         assert np.array_equal(g_v[b][:, rows], hc.v[b][:, rows]), ("v", b)
         assert np.all(g_v[b][:, other] == SENTINEL), ("v untouched", b)
-    if slab:
+    if slab == 2:  # slab + full rows: the slab, then every channel in the standard order
+        lo_s, hi_s = O.standard_to_slab(lo, dom), O.standard_to_slab(hi, dom)
+        for t, l_, h_ in ((cache_k, lo_s[0], hi_s[0]), (cache_rest, lo, hi)):
+            g = _host(t)
+            for b in range(w.shape[0]):
+                rows = np.nonzero(w[b])[0]
+                other = np.nonzero(~w[b])[0]
+                gv = g[b][:, rows]
+                bad = (gv < l_[b][:, rows]) | (gv > h_[b][:, rows])
+                assert not bad.any(), ("slab + full rows", b, int(bad.sum()))
+                assert np.all(g[b][:, other] == SENTINEL), ("k untouched", b)
+    elif slab:
         parts = [(cache_k, 0)] + ([(cache_rest, 1)] if cache_rest is not None else [])
         lo_s, hi_s = O.standard_to_slab(lo, dom), O.standard_to_slab(hi, dom)
         for t, which in parts:
@@ -120,11 +131,13 @@ APPEND_CASES = [
     ("f32", 64, False, 8),
     ("bf16", 128, True, 64),   # every pair dominant: no rest slab
     ("bf16", 64, True, 1),
+    ("bf16", 128, 2, 16),      # slab + full rows
+    ("f32", 64, 2, 4),
 ]
 
 
 @pytest.mark.parametrize("dtype,d,slab,n_dom", APPEND_CASES,
-                         ids=[f"{c[0]}-d{c[1]}-{'slab' if c[2] else 'std'}-n{c[3]}"
+                         ids=[f"{c[0]}-d{c[1]}-{['std', 'slab', 'slab-full'][int(c[2])]}-n{c[3]}"
                               for c in APPEND_CASES])
 def test_kv_cache_append(sa, dtype, d, slab, n_dom):
     say(f"case: kv append {dtype} d={d} slab={slab} n_dom={n_dom}")
@@ -134,8 +147,9 @@ def test_kv_cache_append(sa, dtype, d, slab, n_dom):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     kd = 2 * n_dom if slab else d
     k_cache = torch.full((B, Hkv, Lmax, kd), SENTINEL, dtype=tdt, device=DEV)
-    k_rest = (torch.full((B, Hkv, Lmax, d - kd), SENTINEL, dtype=tdt, device=DEV)
-              if slab and kd < d else None)
+    rest_w = d if slab == 2 else d - kd
+    k_rest = (torch.full((B, Hkv, Lmax, rest_w), SENTINEL, dtype=tdt, device=DEV)
+              if slab and rest_w > 0 else None)
     v_cache = torch.full((B, Hkv, Lmax, d), SENTINEL, dtype=tdt, device=DEV)
     hc = HostCache(B, Hkv, Lmax, d)
     # first call: 37 tokens per row at ragged starts, the last row running past Lmax;
@@ -147,7 +161,7 @@ def test_kv_cache_append(sa, dtype, d, slab, n_dom):
         start = torch.tensor(starts, dtype=torch.int32, device=DEV)
         sa.sa_kv_cache_append(_dev(k_new, dtype), _dev(v_new, dtype), start, k_cache, v_cache,
                               theta=theta, k_rest=k_rest, dom_pairs=domt if slab else None,
-                              slab=slab)
+                              slab=bool(slab), full_rows=slab == 2)
         for b in range(B):
             hc.append(b, k_new[b], v_new[b], starts[b], theta)
     torch.cuda.synchronize()
@@ -181,15 +195,17 @@ def test_kv_cache_append_standard_matches_rope_apply(sa):
         assert np.all((g >= lo) & (g <= hi))
 
 
-@pytest.mark.parametrize("slab,host_rest", [(False, False), (True, False), (True, True)],
-                         ids=["std", "slab", "slab-host-rest"])
-def test_prefill_decode_handoff(sa, slab, host_rest):
+@pytest.mark.parametrize("slab,host_rest,full_rows",
+                         [(False, False, False), (True, False, False), (True, True, False),
+                          (True, False, True)],
+                         ids=["std", "slab", "slab-host-rest", "slab-full-rows"])
+def test_prefill_decode_handoff(sa, slab, host_rest, full_rows):
     """Two prompts (2048 and 1536 tokens) through the prefill layer into one
     cache, then 3 decode steps with per-row positions, each against the oracle.
     With host_rest the non-dominant keys and the values live in pinned host
     memory (FASA-M) and are written and read over the host link."""
     from long_context_sparse_apply_amd.pipeline import DecodeCache
-    say(f"case: prefill -> decode handoff slab={slab} host_rest={host_rest}")
+    say(f"case: prefill -> decode handoff slab={slab} host_rest={host_rest} full_rows={full_rows}")
     lens0 = [2048, 1536]
     T, top_k, n_dom = 3, 256, 16
     base = W.C2.with_(Hq=8, Hkv=2, needle_pairs=4)
@@ -197,13 +213,16 @@ def test_prefill_decode_handoff(sa, slab, host_rest):
     Lmax = max(lens0) + T
     dom = _dom(Hkv, d, n_dom, 32)
     cache = DecodeCache(B, Hkv, Lmax, d, dtype=torch.bfloat16, device=DEV, theta=theta,
-                        dom_pairs=torch.from_numpy(dom).to(DEV), slab=slab, host_rest=host_rest)
+                        dom_pairs=torch.from_numpy(dom).to(DEV), slab=slab, host_rest=host_rest,
+                        full_rows=full_rows)
     if host_rest:
         assert not cache.v.is_cuda and cache.v.is_pinned() and cache.k_rest.is_pinned()
+    second = cache.k_full if full_rows else cache.k_rest
     cache.k.fill_(SENTINEL)
     cache.v.fill_(SENTINEL)
-    if cache.k_rest is not None:
-        cache.k_rest.fill_(SENTINEL)
+    if second is not None:
+        second.fill_(SENTINEL)
+    layout = 2 if full_rows else int(slab)
     hc = HostCache(B, Hkv, Lmax, d)
     for b, S in enumerate(lens0):
         cfg = base.with_(S=S, seed=50 + b)
@@ -217,7 +236,7 @@ def test_prefill_decode_handoff(sa, slab, host_rest):
         hc.append(b, k[0], v[0], 0, theta)
         del layer
     assert cache.lens.cpu().tolist() == lens0
-    _check_cache(cache.k, cache.k_rest, cache.v, hc, "bf16", dom, slab)
+    _check_cache(cache.k, second, cache.v, hc, "bf16", dom, layout)
     dcfg = W.C5.with_(B=B, Hq=Hq, Hkv=Hkv, L=Lmax, d=d, theta=theta, n_dom=n_dom, k=top_k,
                       slab=int(slab))
     lens = np.array(lens0, np.int32)
@@ -239,7 +258,7 @@ def test_prefill_decode_handoff(sa, slab, host_rest):
         x = dict(q_raw=q_new, k=k_or, v=hc.v, lens=lens, dom=dom, batches=list(range(B)))
         say(f"  step {t}: lens {lens.tolist()}")
         _compare_decode(dcfg, step, _HostCache(dcfg, x), _all_samples(dcfg, range(B)), k_amb=hi - lo)
-    _check_cache(cache.k, cache.k_rest, cache.v, hc, "bf16", dom, slab)
+    _check_cache(cache.k, second, cache.v, hc, "bf16", dom, layout)
 
 
 def test_decode_host_placement(sa):
@@ -250,7 +269,7 @@ def test_decode_host_placement(sa):
     import synth.device as SD
     from long_context_sparse_apply_amd.pipeline import DecodeStep
     from tests.test_gpu_end_to_end import _decode_step
-    cfg = W.C5.with_(B=2, L=8192, k=256, ragged=1000)
+    cfg = W.C5.with_(B=2, L=8192, k=256, ragged=1000, full_rows=0)
     say("case: decode with host-placed k_rest / v (slab-8k)")
     x = W.decode_inputs_host(cfg)
     dt = SD.decode_tensors(cfg)
