@@ -6,106 +6,154 @@
 // calibrated band logits are one dot product over all channels of the
 // calibrated pooled vectors.
 //
-// fp32 FMA keeps the scores well inside 1e-4 relative of an fp64 evaluation.
-// The work is tiny next to attention (Hq * N^2 / 2 * d MACs), so this is a
-// plain LDS-tiled 64x64 kernel; tiles strictly above the diagonal are filled
-// with -inf without loading anything.  The accumulation order over channels
-// is ascending, as before.
+// The work is small next to attention (Hq * N^2 / 2 * d MACs) and runs on
+// the bf16 matrix cores in split form (below); tiles strictly above the
+// diagonal are filled with -inf without loading anything.
 #include "sa_common.hpp"
 
 namespace sa {
 
-constexpr int kTile = 64;
-constexpr int kKc = 64;   // channels per LDS stage
-constexpr int kLd = kKc + 4;
+// ------------------------------------------------------------------ split-bf16 matrix-core form
+// Pooled vectors are fp32; each value x is split into three bf16 parts
+// hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid), so that
+// x = hi + mid + lo to within 2^-27 |x| (each rounding keeps 8 significant
+// bits of what is left), and the product <a, b> is summed from the six part
+// products down to 2^-18 of |a b| (hi.hi, hi.mid, mid.hi, hi.lo, lo.hi,
+// mid.mid; the dropped ones are below 2^-27 |a b|) on the matrix cores with
+// fp32 accumulation, smallest first: the split-bf16 scheme of Henry, Tang &
+// Heinecke (2019).  A channel product is then within about 2^-25 of exact,
+// like an fp32 product.  Two parts (the three-product form) leave 2^-17 of
+// |a b| per channel, which a score that nearly cancels can amplify past a
+// 1e-4 relative bound.  One work-group per 64 x 64 output tile: its 64
+// pooled query rows and 64 pooled key rows are staged in LDS with coalesced
+// 16-byte loads (rows padded so a fragment read is bank-conflict free), then
+// one wave per 32 x 32 quarter runs v_mfma_f32_32x32x16_bf16 with A = query
+// rows (lane l: row l % 32, channels 8 (l / 32) .. + 7 of the k-step) and
+// B = key rows (lane l: row l % 32); the C layout gives lane l the output
+// column l % 32 and rows 8 (r / 4) + 4 (l / 32) + r % 4.  Reading fragments
+// straight from global memory instead (32 rows per load instruction) took
+// as long as the fp32 FMA form.
+typedef __attribute__((ext_vector_type(8))) __bf16 bs_bf16x8;
+typedef __attribute__((ext_vector_type(16))) float bs_f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned int bs_u32x4;
 
-// One work-group per 64 x 64 output tile.  The two 64-row slabs of pooled
-// vectors go through LDS in stages of 64 channels with 16-byte loads; each
-// thread accumulates a 4 x 4 block, channels in ascending order.  Rows are
-// padded by 4 floats so the 16 row groups of a read fall in different bank
-// quads.
-__global__ __launch_bounds__(256) void block_gemm_kernel(const float* __restrict__ pq,
-                                                         const float* __restrict__ pk, int Hq,
-                                                         int Hkv, int N, int d, float scale,
-                                                         int causal, float* __restrict__ scores) {
-  const int ti = blockIdx.x;  // tile of I
-  const int tj = blockIdx.y;  // tile of J
-  const int bh = blockIdx.z;
-  const int h = bh % Hq;
-  const int b = bh / Hq;
-  const int g = h / (Hq / Hkv);
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  const int i0 = ti * kTile, j0 = tj * kTile;
+__device__ __forceinline__ uint32_t bs_pack(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 fp32 values -> their bf16 high, middle and low parts (RNE each); the
+// subtractions are exact (each removes the leading bits just rounded off)
+__device__ __forceinline__ void bs_split(const float4& x, const float4& y, bs_bf16x8& hi,
+                                         bs_bf16x8& mid, bs_bf16x8& lo) {
+  float v[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+  bs_u32x4 part[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = bs_pack(v[2 * j], v[2 * j + 1]);
+      part[p][j] = w;
+      if (p < 2) {
+        v[2 * j] -= __uint_as_float(w << 16);
+        v[2 * j + 1] -= __uint_as_float(w & 0xffff0000u);
+      }
+    }
+  hi = __builtin_bit_cast(bs_bf16x8, part[0]);
+  mid = __builtin_bit_cast(bs_bf16x8, part[1]);
+  lo = __builtin_bit_cast(bs_bf16x8, part[2]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void block_gemm_mfma_kernel(const float* __restrict__ pq,
+                                                              const float* __restrict__ pk, int Hq,
+                                                              int Hkv, int N, float scale,
+                                                              int causal,
+                                                              float* __restrict__ scores) {
+  constexpr int KS = D / 16;
+  constexpr int LD = D + 4;         // padded row: 16 rows of a fragment read hit distinct banks
+  constexpr int F4 = D / 4;         // float4 per row
+  const int ti = blockIdx.x, tj = blockIdx.y, bh = blockIdx.z;
+  const int h = bh % Hq, b = bh / Hq, g = h / (Hq / Hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int ti0 = ti * 64, tj0 = tj * 64;
   float* out = scores + static_cast<int64_t>(bh) * N * N;
-
-  if (causal && j0 > i0 + kTile - 1) {
-    for (int e = threadIdx.x; e < kTile * kTile; e += 256) {
-      const int i = i0 + e / kTile, j = j0 + e % kTile;
+  if (causal && tj0 > ti0 + 63) {  // the whole tile lies above the diagonal: no loads
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int i = ti0 + e / 64, j = tj0 + e % 64;
       if (i < N && j < N) out[static_cast<int64_t>(i) * N + j] = -INFINITY;
     }
     return;
   }
-
-  __shared__ __attribute__((aligned(16))) float sa_[kTile * kLd];
-  __shared__ __attribute__((aligned(16))) float sb_[kTile * kLd];
-  const float* A = pq + (static_cast<int64_t>(b) * Hq + h) * N * d;
-  const float* Bm = pk + (static_cast<int64_t>(b) * Hkv + g) * N * d;
-
-  float acc[4][4];
+  // the tile's 64 query rows and 64 key rows, staged with coalesced 16-byte loads
+  __shared__ __attribute__((aligned(16))) float sA[64 * LD];
+  __shared__ __attribute__((aligned(16))) float sB[64 * LD];
+  const float* A = pq + (static_cast<int64_t>(b) * Hq + h) * N * D;
+  const float* Bm = pk + (static_cast<int64_t>(b) * Hkv + g) * N * D;
+  {
+    float4 a[64 * F4 / 256], c[64 * F4 / 256];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
-
-  constexpr int q4 = kKc / 4;  // float4 per staged row
-  for (int k0 = 0; k0 < d; k0 += kKc) {
-    for (int e = threadIdx.x; e < kTile * q4; e += 256) {
-      const int r = e / q4, c4 = e % q4;
-      const int i = i0 + r, j = j0 + r;
-      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 av = i < N ? *reinterpret_cast<const float4*>(A + static_cast<int64_t>(i) * d + k0 + 4 * c4) : z;
-      const float4 bv = j < N ? *reinterpret_cast<const float4*>(Bm + static_cast<int64_t>(j) * d + k0 + 4 * c4) : z;
-      *reinterpret_cast<float4*>(sa_ + r * kLd + 4 * c4) = av;
-      *reinterpret_cast<float4*>(sb_ + r * kLd + 4 * c4) = bv;
+    for (int u = 0; u < 64 * F4 / 256; ++u) {
+      const int e = tid + 256 * u, r = e / F4, q4 = e % F4;
+      a[u] = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(min(ti0 + r, N - 1)) * D + 4 * q4);
+      c[u] = *reinterpret_cast<const float4*>(Bm + static_cast<int64_t>(min(tj0 + r, N - 1)) * D + 4 * q4);
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int cc = 0; cc < kKc; cc += 4) {
-      float4 av[4], bv[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) av[x] = *reinterpret_cast<const float4*>(sa_ + (ty + 16 * x) * kLd + cc);
-#pragma unroll
-      for (int y = 0; y < 4; ++y) bv[y] = *reinterpret_cast<const float4*>(sb_ + (tx + 16 * y) * kLd + cc);
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          acc[x][y] = fmaf(av[x].x, bv[y].x, acc[x][y]);
-          acc[x][y] = fmaf(av[x].y, bv[y].y, acc[x][y]);
-          acc[x][y] = fmaf(av[x].z, bv[y].z, acc[x][y]);
-          acc[x][y] = fmaf(av[x].w, bv[y].w, acc[x][y]);
-        }
+    for (int u = 0; u < 64 * F4 / 256; ++u) {
+      const int e = tid + 256 * u, r = e / F4, q4 = e % F4;
+      *reinterpret_cast<float4*>(sA + r * LD + 4 * q4) = a[u];
+      *reinterpret_cast<float4*>(sB + r * LD + 4 * q4) = c[u];
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  const int i0 = ti0 + 32 * (w >> 1);   // this wave's 32 rows (I)
+  const int j0 = tj0 + 32 * (w & 1);    // and 32 columns (J)
+  if (causal && j0 > i0 + 31) {  // this quarter lies above the diagonal
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = i0 + 8 * (r >> 2) + 4 * hi + (r & 3), j = j0 + l32;
+      if (i < N && j < N) out[static_cast<int64_t>(i) * N + j] = -INFINITY;
+    }
+    return;
+  }
+  const float* ar = sA + (32 * (w >> 1) + l32) * LD + 8 * hi;
+  const float* br = sB + (32 * (w & 1) + l32) * LD + 8 * hi;
+  bs_f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    bs_bf16x8 ah, am, al, bh_, bm, bl;
+    bs_split(*reinterpret_cast<const float4*>(ar + 16 * s), *reinterpret_cast<const float4*>(ar + 16 * s + 4),
+             ah, am, al);
+    bs_split(*reinterpret_cast<const float4*>(br + 16 * s), *reinterpret_cast<const float4*>(br + 16 * s + 4),
+             bh_, bm, bl);
+    // C[m = I row][n = J column]: A = query rows, B = key rows; small parts first
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bm, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh_, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bh_, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bm, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh_, acc, 0, 0, 0);
   }
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int i = i0 + ty + 16 * x;
-    if (i >= N) continue;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int j = j0 + tx + 16 * y;
-      if (j >= N) continue;
-      out[static_cast<int64_t>(i) * N + j] = (causal && j > i) ? -INFINITY : scale * acc[x][y];
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int i = i0 + 8 * (r >> 2) + 4 * hi + (r & 3), j = j0 + l32;
+    if (i < N && j < N)
+      out[static_cast<int64_t>(i) * N + j] = (causal && j > i) ? -INFINITY : scale * acc[r];
   }
 }
 
 hipError_t launch_block_gemm(const float* pq, const float* pk, int B, int Hq, int Hkv, int N,
                              int d, float scale, int causal, float* scores, hipStream_t st) {
-  const int t = (N + kTile - 1) / kTile;
+  const int t = (N + 63) / 64;
   const dim3 grid(t, t, static_cast<unsigned>(B * Hq));
-  block_gemm_kernel<<<grid, 256, 0, st>>>(pq, pk, Hq, Hkv, N, d, scale, causal, scores);
+  if (d == 128)
+    block_gemm_mfma_kernel<128><<<grid, 256, 0, st>>>(pq, pk, Hq, Hkv, N, scale, causal, scores);
+  else
+    block_gemm_mfma_kernel<64><<<grid, 256, 0, st>>>(pq, pk, Hq, Hkv, N, scale, causal, scores);
   return hipGetLastError();
 }
 
