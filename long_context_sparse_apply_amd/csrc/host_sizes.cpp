@@ -53,6 +53,13 @@ size_t topk_lds_bytes(int cols, int cap) {
   return static_cast<size_t>(cap) * 8 + kBins * 4 + words * 4 + (kLongThreads / kWave + 4) * 4;
 }
 
+// LDS of a fused-selection work-group: the candidate / bitmap region, the
+// radix histogram and the scan scalars.
+size_t token_select_lds_bytes(int cols, int cap) {
+  return static_cast<size_t>(token_select_region(cols, cap)) + kBins * 4 +
+         (kLongThreads / kWave + 4) * 4;
+}
+
 // Candidate buffer of a long row: k plus a quarter plus 1024 (the sampled
 // threshold overshoots k by a few standard deviations), at most kMaxCap.
 int topk_cap(int k) {

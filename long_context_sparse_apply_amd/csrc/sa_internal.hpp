@@ -63,6 +63,7 @@ hipError_t launch_token_collect(const void* q, const void* k, int dtype, int B, 
 size_t token_topk_ws_bytes(int64_t rows, int Lmax);
 // long-row top-k: LDS of a work-group, candidate buffer of a row (plain and fused)
 size_t topk_lds_bytes(int cols, int cap);
+size_t token_select_lds_bytes(int cols, int cap);
 int topk_cap(int k);
 int token_topk_cap(int k);
 hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,

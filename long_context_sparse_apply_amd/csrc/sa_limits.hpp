@@ -27,4 +27,15 @@ constexpr int kCollectTile = 4096;
 constexpr int kCollectWaves = 4;
 constexpr int kCollectSlots = 256;
 
+// fused selection's LDS region: the candidate buffer (cap 64-bit composites)
+// or, on the exact fallback, the row's selection bitmap followed by a buffer
+// of at least kSelFallbackBuf composites (bytes, a multiple of 16)
+constexpr int kSelFallbackBuf = 2048;
+constexpr long long token_select_region(int cols, int cap) {
+  const long long bitmap = ((static_cast<long long>(cols) + 31) / 32 * 4 + 15) / 16 * 16;
+  const long long a = static_cast<long long>(cap) * 8;
+  const long long b = bitmap + static_cast<long long>(kSelFallbackBuf) * 8;
+  return a > b ? a : b;
+}
+
 }  // namespace sa

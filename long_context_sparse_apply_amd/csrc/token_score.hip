@@ -65,7 +65,12 @@ struct TokenScoreShape {
 // passes its row's threshold key (and lies below cache_len) to the wave's own
 // candidate list of that row and tile (blockIdx.x), as (score bits << 32 |
 // token); the wave counts in scalars and writes its counts at the end
-// (entries past the slots are dropped, the count stays true).
+// (entries past the slots are dropped, the count stays true).  In this mode
+// a chunk's CT rows are CT/64 runs of 64 tokens, run s from segment s of the
+// tile (the tile split into CT/64 equal segments, walked 64 tokens a chunk),
+// and row r belongs to wave (r / 64) mod (CT / 64) of its head group, so each
+// wave's list is in ascending token order and a row's lists, taken in (tile,
+// wave) order, are too.
 template <typename T, int ROW, int GRP, int NDC, bool SLAB, bool COLLECT>
 __global__ __launch_bounds__(256) void token_score_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int Hq, int Hkv, int Lmax, int d,
@@ -75,6 +80,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   constexpr int ES = Sh::ES, ROWB = Sh::ROWB, CPR = Sh::CPR, CT = Sh::CT, HPT = Sh::HPT;
   constexpr int CHB = Sh::CHB, LPW = Sh::LPW;
   static_assert(!SLAB || ROW == NDC, "the slab row is exactly the dominant channels");
+  static_assert(!COLLECT || CT % 64 == 0, "collect mode takes chunks of whole 64-token runs");
   __shared__ __attribute__((aligned(1024))) uint8_t sk0[CHB];
   __shared__ __attribute__((aligned(1024))) uint8_t sk1[CHB];
   // collect mode with chunks of at most 16 KB: a third stage
@@ -92,31 +98,41 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   const int L = cache_len[b];
   const int ndc = 2 * n_dom;
   const int tb = blockIdx.x * chunks_per_wg * CT;                   // first token of this WG
-  int nch = (Lmax - tb + CT - 1) / CT;
+  // chunks holding a token below Lmax (collect mode: segment 0 has the most)
+  int nch = COLLECT ? (Lmax - tb + 63) / 64 : (Lmax - tb + CT - 1) / CT;
   nch = nch < chunks_per_wg ? nch : chunks_per_wg;
   const uint8_t* kb = reinterpret_cast<const uint8_t*>(k + (static_cast<int64_t>(b) * Hkv + g) * Lmax * ROW);
 
-  // stage chunk c's rows (rows past the cache end re-read its last row); the
-  // collect instances load through a buffer resource over this (b, KV head)'s
-  // rows (at most 64 MiB), whose LDS writes the compiler tracks per buffer
+  // the token in row `row` of chunk c (collect mode: runs of 64 tokens from
+  // the tile's CT/64 segments; scoring: CT consecutive tokens)
+  const int seg_tokens = chunks_per_wg * 64;
+  auto chunk_token = [&](int c, int row) {
+    if constexpr (COLLECT)
+      return tb + (row >> 6) * seg_tokens + c * 64 + (row & 63);
+    else
+      return tb + c * CT + row;
+  };
+  // stage chunk c's rows (tokens past the cache end re-read its last row);
+  // the collect instances load through a buffer resource over this (b, KV
+  // head)'s rows (at most 64 MiB), whose LDS writes the compiler tracks per
+  // buffer
   const auto rsrc = buffer_rsrc(kb, Lmax * ROWB);
-  auto issue_one = [&](int t0, int last, int j, uint8_t* buf) {
+  auto issue_one = [&](int c, int j, uint8_t* buf) {
     const int ins = wid * LPW + j;
     const int off = ins * 1024 + lane * 16;
     const int row = off / ROWB;
     const int pos = (off % ROWB) >> 4;
-    const int src_row = row < last ? row : last;
-    const int byte = (t0 + src_row) * ROWB + ((pos ^ (row % CPR)) << 4);
+    const int tok = chunk_token(c, row);
+    const int src = tok < Lmax ? tok : Lmax - 1;
+    const int byte = src * ROWB + ((pos ^ (row % CPR)) << 4);
     if constexpr (COLLECT)
       lds_dma16_buf(rsrc, byte, buf + ins * 1024);
     else
       lds_dma16(kb + byte, buf + ins * 1024);
   };
   auto issue = [&](int c, uint8_t* buf) {
-    const int t0 = tb + c * CT;
-    const int last = Lmax - 1 - t0;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) issue_one(t0, last, j, buf);
+    for (int j = 0; j < LPW; ++j) issue_one(c, j, buf);
   };
   if (!THREE && nch > 0) issue(0, sk0);
 
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   };
   auto score_chunk = [&](int c, const uint8_t* buf) {
     if (!active) return;
-    const int t = tb + c * CT + r;
+    const int t = chunk_token(c, r);
     const uint8_t* rowp = buf + r * ROWB;
     float kv[NDC];
     if constexpr (SLAB) {

@@ -395,6 +395,54 @@ __device__ void emit_bitmap(const TopkShared& sh, int nwords, int32_t* dst, int 
   if (tid == 0) *count = total;
 }
 
+// The k-th largest composite among cbuf[0, nbuf) (need = k): the MSB-first
+// radix levels of select_in_lds, without marking; every composite at or above
+// the returned value is selected and no other.
+__device__ uint64_t select_bound_in_lds(const TopkShared& sh, int nbuf, int need, uint64_t prefix0,
+                                        int pbits0) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = prefix0;
+  int pbits = pbits0;
+  while (true) {
+    int bsel, above, cntb;
+    auto each = [&](auto f) {
+      for (int i = tid; i < nbuf; i += kLongThreads) f(sh.cbuf[i]);
+    };
+    radix_level(sh, pbits, prefix, need, each, bsel, above, cntb);
+    need -= above;
+    if (cntb == need) {
+      // the lowest composite with this prefix and digit (composites are
+      // unique, so the levels end by the 64th bit)
+      const uint64_t top = pbits == 0 ? 0ull : prefix << (64 - pbits);
+      return top | ((static_cast<uint64_t>(bsel) << (64 - kDigit)) >> pbits);
+    }
+    prefix = (prefix << kDigit) | static_cast<uint64_t>(bsel);
+    pbits += kDigit;
+  }
+}
+
+// The columns of the composites at or above `bound` among cbuf[0, nbuf),
+// which is in ascending column order, into dst[0, max_out) in that order,
+// padded with -1, and their number into *count: a work-group compaction, each
+// thread taking a contiguous run.
+__device__ void emit_ordered(const TopkShared& sh, int nbuf, uint64_t bound, int32_t* dst,
+                             int max_out, int32_t* count) {
+  const int tid = threadIdx.x;
+  const int per = (nbuf + kLongThreads - 1) / kLongThreads;
+  const int i0 = tid * per < nbuf ? tid * per : nbuf;
+  const int i1 = i0 + per < nbuf ? i0 + per : nbuf;
+  int mine = 0;
+  for (int i = i0; i < i1; ++i) mine += sh.cbuf[i] >= bound ? 1 : 0;
+  int total;
+  int pos = block_excl_scan(mine, sh.tmp, total);
+  for (int i = i0; i < i1; ++i) {
+    const uint64_t c = sh.cbuf[i];
+    if (c >= bound) dst[pos++] = comp_col(c);
+  }
+  for (int p = total + tid; p < max_out; p += kLongThreads) dst[p] = -1;
+  if (tid == 0) *count = total;
+}
+
 // One 512-thread work-group per row.
 //  1. Samples: kSegs contiguous segments spread over the candidate columns
 //     (up to 16384 values, read once and kept in registers); the
@@ -844,100 +892,124 @@ __global__ __launch_bounds__(kLongThreads) void token_select_kernel(
   static_assert(kMaxLists <= kLongThreads, "a thread a list in the count scan");
   __shared__ int s_at[kMaxLists], s_cn[kMaxLists];  // each list's place and length
   __shared__ uint64_t s_lo[kLongThreads / kWave], s_hi[kLongThreads / kWave];
-  const TopkShared sh = topk_views(topk_lds, Lmax, cap);
+  // LDS: the region (candidates, or bitmap + buffer on the fallback), the
+  // radix histogram, the scan scalars
+  const int region = static_cast<int>(token_select_region(Lmax, cap));
+  TopkShared sh;
+  sh.cbuf = reinterpret_cast<uint64_t*>(topk_lds);
+  sh.hist = reinterpret_cast<uint32_t*>(topk_lds + region);
+  sh.bitmap = nullptr;
+  sh.tmp = reinterpret_cast<int*>(sh.hist + kBins);
+  sh.pick = sh.tmp + kLongThreads / kWave;
+  sh.nbuf = sh.pick + 2;
+  sh.cap = cap;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / Hq);
   const int g = static_cast<int>(row % Hq) / (Hq / Hkv);
   const int n = clamp_len(cache_len[b], Lmax);
   const int k = k_top;
-  const int nwords = (n + 31) / 32;
-  for (int w = tid; w < nwords; w += kLongThreads) sh.bitmap[w] = 0u;
-  if (tid == 0) *sh.nbuf = 0;
-  __syncthreads();
+  int32_t* dst = idx_out + row * max_out;
+  // (n <= k <= max_out here)
   if (k >= n) {
-    for (int i = tid; i < n; i += kLongThreads) atomicOr(&sh.bitmap[i >> 5], 1u << (i & 31));
-  } else if (k > 0) {
-    // gather the (tile, wave) lists: thread j < nsub owns list j
-    const int nsub = col.tiles * kCollectWaves;  // <= kLongThreads (Lmax <= 262144)
-    const int cj = tid < nsub ? col.cnt[row * nsub + tid] : 0;
-    const bool over = __syncthreads_or(cj > kCollectSlots);
-    int total;
-    const int at = block_excl_scan(cj, sh.tmp, total);
-    if (!over && total >= k && total <= cap) {
-      // Four threads a list, each taking every fourth entry; a round issues
-      // all its loads before any store (a list past 64 entries takes more
-      // rounds; a round's reads stay in the list's kCollectSlots slots).  The
-      // smallest and largest composite come along for the select.
-      if (tid < nsub) {
-        s_at[tid] = at;
-        s_cn[tid] = cj;
-      }
-      __syncthreads();
-      uint64_t lo = ~0ull, hi = 0ull;
-      for (int j = tid >> 2; j < nsub; j += kLongThreads / 4) {
-        const int nj = s_cn[j], aj = s_at[j];
-        const uint64_t* src = col.cand + (row * nsub + j) * kCollectSlots + (tid & 3);
-        for (int base = 0; base < nj; base += 64) {
-          uint64_t v[16];
+    for (int p = tid; p < max_out; p += kLongThreads) dst[p] = p < n ? p : -1;
+    if (tid == 0) count_out[row] = n;
+    return;
+  }
+  if (k <= 0) {
+    for (int p = tid; p < max_out; p += kLongThreads) dst[p] = -1;
+    if (tid == 0) count_out[row] = 0;
+    return;
+  }
+  // gather the (tile, wave) lists: thread j < nsub owns list j
+  const int nsub = col.tiles * kCollectWaves;  // <= kLongThreads (Lmax <= 262144)
+  const int cj = tid < nsub ? col.cnt[row * nsub + tid] : 0;
+  const bool over = __syncthreads_or(cj > kCollectSlots);
+  int total;
+  const int at = block_excl_scan(cj, sh.tmp, total);
+  if (!over && total >= k && total <= cap) {
+    // Four threads a list, each taking every fourth entry; a round issues
+    // all its loads before any store (a list past 64 entries takes more
+    // rounds; a round's reads stay in the list's kCollectSlots slots).  The
+    // lists, taken in order, are in ascending token order, and so is the
+    // buffer.  The smallest and largest composite come along for the select.
+    if (tid < nsub) {
+      s_at[tid] = at;
+      s_cn[tid] = cj;
+    }
+    __syncthreads();
+    uint64_t lo = ~0ull, hi = 0ull;
+    for (int j = tid >> 2; j < nsub; j += kLongThreads / 4) {
+      const int nj = s_cn[j], aj = s_at[j];
+      const uint64_t* src = col.cand + (row * nsub + j) * kCollectSlots + (tid & 3);
+      for (int base = 0; base < nj; base += 64) {
+        uint64_t v[16];
 #pragma unroll
-          for (int m = 0; m < 16; ++m) v[m] = src[base + 4 * m];
+        for (int m = 0; m < 16; ++m) v[m] = src[base + 4 * m];
 #pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            const int i = base + (tid & 3) + 4 * m;
-            if (i < nj) {
-              // (score bits, token) -> the composite the selection compares
-              const uint64_t c = composite(order_key(__uint_as_float(static_cast<uint32_t>(v[m] >> 32))),
-                                           static_cast<int>(static_cast<uint32_t>(v[m])));
-              sh.cbuf[aj + i] = c;
-              lo = c < lo ? c : lo;
-              hi = c > hi ? c : hi;
-            }
+        for (int m = 0; m < 16; ++m) {
+          const int i = base + (tid & 3) + 4 * m;
+          if (i < nj) {
+            // (score bits, token) -> the composite the selection compares
+            const uint64_t c = composite(order_key(__uint_as_float(static_cast<uint32_t>(v[m] >> 32))),
+                                         static_cast<int>(static_cast<uint32_t>(v[m])));
+            sh.cbuf[aj + i] = c;
+            lo = c < lo ? c : lo;
+            hi = c > hi ? c : hi;
           }
         }
       }
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) {
-        const uint64_t a = __shfl_xor(lo, o, kWave), c = __shfl_xor(hi, o, kWave);
-        lo = a < lo ? a : lo;
-        hi = c > hi ? c : hi;
-      }
-      if ((tid & (kWave - 1)) == 0) {
-        s_lo[tid / kWave] = lo;
-        s_hi[tid / kWave] = hi;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int w = 0; w < kLongThreads / kWave; ++w) {
-        lo = s_lo[w] < lo ? s_lo[w] : lo;
-        hi = s_hi[w] > hi ? s_hi[w] : hi;
-      }
-      // every candidate lies in [lo, hi], so all share the bits above the
-      // highest bit where lo and hi differ (composites are unique: lo < hi
-      // unless there is one candidate)
-      int pb = __clzll(static_cast<long long>(lo ^ hi));
-      pb = pb > 63 ? 63 : pb;
-      select_in_lds(sh, total, k, pb > 0 ? hi >> (64 - pb) : 0ull, pb);
-    } else {
-      // every token, its score recomputed exactly as the scoring kernel has it
-      stage_query_slice<T, NDC>(s_q, q, row, g, d, dom, n_dom, scale);
-      if (!SLAB) stage_channels<NDC>(s_ch, g, d, dom, n_dom);
-      __syncthreads();
-      const int rowlen = SLAB ? NDC : d;
-      const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * rowlen;
-      auto val = [&](int i) {
-        float kv[NDC];
-        if constexpr (SLAB)
-          load_slab_row<T, NDC>(kb + static_cast<int64_t>(i) * NDC, kv);
-        else
-          load_std_row<T, NDC>(kb + static_cast<int64_t>(i) * d, s_ch, kv);
-        return token_dot<NDC>(s_q, kv);
-      };
-      select_from_source(sh, val, 0, n, k);
     }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      const uint64_t a = __shfl_xor(lo, o, kWave), c = __shfl_xor(hi, o, kWave);
+      lo = a < lo ? a : lo;
+      hi = c > hi ? c : hi;
+    }
+    if ((tid & (kWave - 1)) == 0) {
+      s_lo[tid / kWave] = lo;
+      s_hi[tid / kWave] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kLongThreads / kWave; ++w) {
+      lo = s_lo[w] < lo ? s_lo[w] : lo;
+      hi = s_hi[w] > hi ? s_hi[w] : hi;
+    }
+    // every candidate lies in [lo, hi], so all share the bits above the
+    // highest bit where lo and hi differ (composites are unique: lo < hi
+    // unless there is one candidate)
+    int pb = __clzll(static_cast<long long>(lo ^ hi));
+    pb = pb > 63 ? 63 : pb;
+    const uint64_t bound = select_bound_in_lds(sh, total, k, pb > 0 ? hi >> (64 - pb) : 0ull, pb);
+    emit_ordered(sh, total, bound, dst, max_out, count_out + row);
+    return;
   }
+  // Fallback (a list overflowed, or the candidates are not in [k, cap]: an
+  // unlucky sample): every token, its score recomputed exactly as the scoring
+  // kernel has it.  The row's bitmap sits at the end of the region, the
+  // buffer before it.
+  const int nwords = (n + 31) / 32;
+  const int bm_bytes = ((Lmax + 31) / 32 * 4 + 15) / 16 * 16;
+  sh.bitmap = reinterpret_cast<uint32_t*>(topk_lds + region - bm_bytes);
+  sh.cap = (region - bm_bytes) / 8;
+  for (int w = tid; w < nwords; w += kLongThreads) sh.bitmap[w] = 0u;
+  stage_query_slice<T, NDC>(s_q, q, row, g, d, dom, n_dom, scale);
+  if (!SLAB) stage_channels<NDC>(s_ch, g, d, dom, n_dom);
   __syncthreads();
-  emit_bitmap(sh, nwords, idx_out + row * max_out, max_out, count_out + row);
+  const int rowlen = SLAB ? NDC : d;
+  const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * rowlen;
+  auto val = [&](int i) {
+    float kv[NDC];
+    if constexpr (SLAB)
+      load_slab_row<T, NDC>(kb + static_cast<int64_t>(i) * NDC, kv);
+    else
+      load_std_row<T, NDC>(kb + static_cast<int64_t>(i) * d, s_ch, kv);
+    return token_dot<NDC>(s_q, kv);
+  };
+  select_from_source(sh, val, 0, n, k);
+  __syncthreads();
+  emit_bitmap(sh, nwords, dst, max_out, count_out + row);
 }
 
 // Workspace (sized by token_topk_ws_bytes): thresholds [rows], list counts
@@ -959,7 +1031,7 @@ hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int
   int* cnt = reinterpret_cast<int*>(w + align256(static_cast<size_t>(rows) * 4));
   uint64_t* cand = reinterpret_cast<uint64_t*>(w + align256(static_cast<size_t>(rows) * 4) + align256(lists * 4));
   const TokenCollect col{thr, cnt, cand, tiles};
-  const size_t lds = topk_lds_bytes(Lmax, cap);
+  const size_t lds = token_select_lds_bytes(Lmax, cap);
   // scored slots: exactly 2 n_dom in the slab, a power of two of at least 8
   // covering them in the standard layout (as the scoring kernel has it)
   const int need = 2 * n_dom;
@@ -974,7 +1046,7 @@ hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int
     const auto* kk = static_cast<const T*>(k);                                                      \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&token_select_kernel<T, C, SL>), \
                                        hipFuncAttributeMaxDynamicSharedMemorySize,                  \
-                                       static_cast<int>(topk_lds_bytes(kMaxLongCols, kMaxCap)));    \
+                                       static_cast<int>(token_select_lds_bytes(kMaxLongCols, kMaxCap))); \
     if (e != hipSuccess) return e;                                                                  \
     switch (grp) {                                                                                  \
       case 1: SA_TT_G(T, C, SL, 1); break;                                                          \
