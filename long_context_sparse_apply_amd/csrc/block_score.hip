@@ -25,9 +25,10 @@ namespace sa {
 // like an fp32 product.  Two parts (the three-product form) leave 2^-17 of
 // |a b| per channel, which a score that nearly cancels can amplify past a
 // 1e-4 relative bound.  One work-group per 64 x 64 output tile: its 64
-// pooled query rows and 64 pooled key rows are staged in LDS with coalesced
-// 16-byte loads (rows padded so a fragment read is bank-conflict free), then
-// one wave per 32 x 32 quarter runs v_mfma_f32_32x32x16_bf16 with A = query
+// pooled query rows and 64 pooled key rows are staged in LDS 64 channels at
+// a time with coalesced 16-byte loads (rows padded so a fragment read is
+// bank-conflict free; 34 KB of LDS, four work-groups a CU), and after each
+// stage one wave per 32 x 32 quarter runs v_mfma_f32_32x32x16_bf16 with A = query
 // rows (lane l: row l % 32, channels 8 (l / 32) .. + 7 of the k-step) and
 // B = key rows (lane l: row l % 32); the C layout gives lane l the output
 // column l % 32 and rows 8 (r / 4) + 4 (l / 32) + r % 4.  Reading fragments
@@ -71,9 +72,6 @@ __global__ __launch_bounds__(256) void block_gemm_mfma_kernel(const float* __res
                                                               int Hkv, int N, float scale,
                                                               int causal,
                                                               float* __restrict__ scores) {
-  constexpr int KS = D / 16;
-  constexpr int LD = D + 4;         // padded row: 16 rows of a fragment read hit distinct banks
-  constexpr int F4 = D / 4;         // float4 per row
   const int ti = blockIdx.x, tj = blockIdx.y, bh = blockIdx.z;
   const int h = bh % Hq, b = bh / Hq, g = h / (Hq / Hkv);
   const int tid = threadIdx.x;
@@ -89,18 +87,30 @@ __global__ __launch_bounds__(256) void block_gemm_mfma_kernel(const float* __res
     }
     return;
   }
-  // the tile's 64 query rows and 64 key rows, staged with coalesced 16-byte loads
+  // the tile's 64 query rows and 64 key rows, staged KC channels at a time
+  // with coalesced 16-byte loads (64 channels: two stages at d = 128)
+  constexpr int KC = D < 64 ? D : 64;
+  constexpr int LD = KC + 4;        // padded row: 16 rows of a fragment read hit distinct banks
+  constexpr int F4 = KC / 4;        // float4 per staged row
   __shared__ __attribute__((aligned(16))) float sA[64 * LD];
   __shared__ __attribute__((aligned(16))) float sB[64 * LD];
   const float* A = pq + (static_cast<int64_t>(b) * Hq + h) * N * D;
   const float* Bm = pk + (static_cast<int64_t>(b) * Hkv + g) * N * D;
-  {
+  const int i0 = ti0 + 32 * (w >> 1);   // this wave's 32 rows (I)
+  const int j0 = tj0 + 32 * (w & 1);    // and 32 columns (J)
+  const bool live = !(causal && j0 > i0 + 31);  // this quarter lies on or below the diagonal
+  const float* ar = sA + (32 * (w >> 1) + l32) * LD + 8 * hi;
+  const float* br = sB + (32 * (w & 1) + l32) * LD + 8 * hi;
+  bs_f32x16 acc = {};
+#pragma unroll
+  for (int c0 = 0; c0 < D; c0 += KC) {
+    if (c0 > 0) __syncthreads();  // every wave is done with the previous stage
     float4 a[64 * F4 / 256], c[64 * F4 / 256];
 #pragma unroll
     for (int u = 0; u < 64 * F4 / 256; ++u) {
       const int e = tid + 256 * u, r = e / F4, q4 = e % F4;
-      a[u] = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(min(ti0 + r, N - 1)) * D + 4 * q4);
-      c[u] = *reinterpret_cast<const float4*>(Bm + static_cast<int64_t>(min(tj0 + r, N - 1)) * D + 4 * q4);
+      a[u] = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(min(ti0 + r, N - 1)) * D + c0 + 4 * q4);
+      c[u] = *reinterpret_cast<const float4*>(Bm + static_cast<int64_t>(min(tj0 + r, N - 1)) * D + c0 + 4 * q4);
     }
 #pragma unroll
     for (int u = 0; u < 64 * F4 / 256; ++u) {
@@ -108,35 +118,34 @@ __global__ __launch_bounds__(256) void block_gemm_mfma_kernel(const float* __res
       *reinterpret_cast<float4*>(sA + r * LD + 4 * q4) = a[u];
       *reinterpret_cast<float4*>(sB + r * LD + 4 * q4) = c[u];
     }
+    __syncthreads();
+    {
+      // (a quarter above the diagonal, only on diagonal tiles, computes too
+      // and writes -inf below: no branch around the matrix products)
+#pragma unroll
+      for (int s = 0; s < KC / 16; ++s) {
+        bs_bf16x8 ah, am, al, bh_, bm, bl;
+        bs_split(*reinterpret_cast<const float4*>(ar + 16 * s), *reinterpret_cast<const float4*>(ar + 16 * s + 4),
+                 ah, am, al);
+        bs_split(*reinterpret_cast<const float4*>(br + 16 * s), *reinterpret_cast<const float4*>(br + 16 * s + 4),
+                 bh_, bm, bl);
+        // C[m = I row][n = J column]: A = query rows, B = key rows; small parts first
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bm, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh_, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bh_, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bm, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh_, acc, 0, 0, 0);
+      }
+    }
   }
-  __syncthreads();
-  const int i0 = ti0 + 32 * (w >> 1);   // this wave's 32 rows (I)
-  const int j0 = tj0 + 32 * (w & 1);    // and 32 columns (J)
-  if (causal && j0 > i0 + 31) {  // this quarter lies above the diagonal
+  if (!live) {  // a quarter above the diagonal
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = i0 + 8 * (r >> 2) + 4 * hi + (r & 3), j = j0 + l32;
       if (i < N && j < N) out[static_cast<int64_t>(i) * N + j] = -INFINITY;
     }
     return;
-  }
-  const float* ar = sA + (32 * (w >> 1) + l32) * LD + 8 * hi;
-  const float* br = sB + (32 * (w & 1) + l32) * LD + 8 * hi;
-  bs_f32x16 acc = {};
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    bs_bf16x8 ah, am, al, bh_, bm, bl;
-    bs_split(*reinterpret_cast<const float4*>(ar + 16 * s), *reinterpret_cast<const float4*>(ar + 16 * s + 4),
-             ah, am, al);
-    bs_split(*reinterpret_cast<const float4*>(br + 16 * s), *reinterpret_cast<const float4*>(br + 16 * s + 4),
-             bh_, bm, bl);
-    // C[m = I row][n = J column]: A = query rows, B = key rows; small parts first
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bm, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh_, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bh_, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bm, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh_, acc, 0, 0, 0);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
