@@ -258,8 +258,12 @@ def run_sfa(steps, warmup, torch, flush, S=8192, Hq=32, Hkv=8, d=128, kf=16):
                        f"k={kf} active channels per token, bf16",
            "codes_us": codes[0], "attend_ms": attend[0] / 1e3,
            "tok_per_s": S / ((codes[0] + attend[0]) * 1e-6),
-           "attend_tflops": flops / (attend[0] * 1e-6) / 1e12,
-           "attend_mfma_frac": flops / (attend[0] * 1e-6) / PEAK_BF16_FLOPS}
+           # the dense matrix-unit work the kernel performs over the zero-filled
+           # codes (4 d per visible pair), not the method's intersection work
+           # (about (k/d)^2 of it), so a rate of the kernel, not of SFA
+           "attend_dense_equiv_tflops": flops / (attend[0] * 1e-6) / 1e12,
+           "attend_dense_equiv_mfma_frac": flops / (attend[0] * 1e-6) / PEAK_BF16_FLOPS,
+           "intersection_flops_share": (kf / d) ** 2}
     del layer, q, k, v
     torch.cuda.empty_cache()
     return res
