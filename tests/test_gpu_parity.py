@@ -107,6 +107,16 @@ BLOCK_CASES = [
                                           needle_keys=0, calibrate=0), None),
     ("single-band-block256", W.C2.with_(S=256 * 12, Hq=4, Hkv=1, block=256, band_split_pair=0,
                                         needle_pairs=0), None),
+    # the pooling pass's other thread shapes: 512 threads with one row a
+    # thread (d 64, block 128), two rows (fp32 d 64, block 256) and four rows
+    # (fp32 d 128, block 256); 256 threads over a block of 16 rows (half of
+    # them idle)
+    ("d64-bf16-block128", W.C1.with_(dtype="bf16", S=128 * 20, Hq=4, Hkv=2, block=128,
+                                     needle_keys=0), None),
+    ("d64-f32-block256", W.C1.with_(S=256 * 6, Hq=2, Hkv=1, block=256, needle_keys=0), None),
+    ("d128-f32-block256", W.C2.with_(dtype="f32", S=256 * 5, Hq=4, Hkv=2, block=256,
+                                     needle_pairs=0), None),
+    ("d128-bf16-block16", W.C2.with_(S=16 * 90, Hq=4, Hkv=1, block=16, needle_pairs=0), None),
 ]
 
 
