@@ -15,7 +15,8 @@
 //
 // Short rows (<= 1024 columns, the prefill block rows): one wave per row, the
 // row in registers (slot j of lane l = column 64 j + l), the k-th key found by
-// a 32-step bitwise search with ballot counts; ties on that key go to the
+// a bitwise search with ballot counts (at most 32 steps; it stops as soon as
+// exactly k keys reach the bits fixed so far); ties on that key go to the
 // lowest columns through a running count in column order.
 //
 // Long rows (the decode token rows, up to 262144 columns): one 512-thread
@@ -84,12 +85,17 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   uint32_t T = 0;
   int need = 0;
   if (k < ncand) {
+    // T: the largest key with at least k candidates at or above it, bit by
+    // bit from the top.  Once exactly k are at or above T the k best are
+    // known (they are the keys >= T) and the lower bits cannot change the
+    // selection, so the search stops there.
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t t = T | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int j = 0; j < E; ++j) cnt += __popcll(__ballot(((candm >> j) & 1u) && key[j] >= t));
       if (cnt >= k) T = t;
+      if (cnt == k) break;
     }
     int gt = 0;
 #pragma unroll
