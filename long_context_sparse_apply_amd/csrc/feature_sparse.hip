@@ -36,7 +36,9 @@ __global__ __launch_bounds__(256) void sfa_sparsify_kernel(const T* __restrict__
   uint32_t T_ = 0;
   int need = 0;
   if (kf < D) {
-    // a bf16 magnitude occupies bits 30..16 of its fp32 pattern: 15 steps
+    // a bf16 magnitude occupies bits 30..16 of its fp32 pattern: at most 15
+    // steps, fewer once exactly kf magnitudes reach the bits fixed so far
+    // (they are then the kept channels whatever the lower bits)
     constexpr int kLowBit = sizeof(T) == 2 ? 16 : 0;
     for (int bit = 30; bit >= kLowBit; --bit) {
       const uint32_t t = T_ | (1u << bit);
@@ -44,6 +46,7 @@ __global__ __launch_bounds__(256) void sfa_sparsify_kernel(const T* __restrict__
 #pragma unroll
       for (int j = 0; j < E; ++j) cnt += __popcll(__ballot(key[j] >= t));
       if (cnt >= kf) T_ = t;
+      if (cnt == kf) break;
     }
     int gt = 0;
 #pragma unroll
