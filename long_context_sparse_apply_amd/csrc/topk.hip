@@ -762,7 +762,12 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
   __syncthreads();
   const int rowlen = SLAB ? NDC : d;
   const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * rowlen;
-  // sample e = tid + j kLongThreads sits at (e / seg_len) seg_stride + e % seg_len
+  // sample e = tid + j kLongThreads sits at (e / seg_len) seg_stride + e % seg_len.
+  // The per-load split of e divides by the uniform seg_len (<= kSegLenF) with
+  // a multiply-high by m = floor((2^32 - 1) / seg_len) + 1: for e < 2^32 /
+  // seg_len its error stays below 1 / seg_len, so the quotient is exact.
+  const uint32_t seg_m = 0xFFFFFFFFu / static_cast<uint32_t>(seg_len) + 1u;
+  auto seg_of = [&](int e) { return static_cast<int>(__umulhi(static_cast<uint32_t>(e), seg_m)); };
   // (segment / offset stepped without a division); a sample past nsamp reads
   // token 0 and its keys are dropped
   const int seg_stride = n / kSegs;
@@ -784,7 +789,8 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
 #pragma unroll
       for (int i = 0; i < R16; ++i) {
         const int e = j * kLongThreads + wv * kWave + i * RPI + rsub;  // the sample loaded
-        const int tok_e = e < nsamp ? (e / seg_len) * seg_stride + e % seg_len : 0;
+        const int se = seg_of(e);
+        const int tok_e = e < nsamp ? se * seg_stride + (e - se * seg_len) : 0;
         raw[i] = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(tok_e) * NDC)[part];
       }
 #pragma unroll
@@ -836,7 +842,8 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
 #pragma unroll
       for (int i = 0; i < kWave / RPI; ++i) {
         const int e = j * kLongThreads + wv * kWave + i * RPI + rsub;  // the sample loaded
-        const int tok_e = e < nsamp ? (e / seg_len) * seg_stride + e % seg_len : 0;
+        const int se = seg_of(e);
+        const int tok_e = e < nsamp ? se * seg_stride + (e - se * seg_len) : 0;
         raw[i] = reinterpret_cast<const uint16_t*>(kb)[static_cast<int64_t>(tok_e) * d + ch];
       }
 #pragma unroll
