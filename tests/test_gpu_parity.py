@@ -438,6 +438,8 @@ DECODE_CASES = [  # name, dtype, B, Hq, Hkv, L, d, n_dom, slab, max_k
     ("bf16-slab", "bf16", 2, 8, 2, 2048, 128, 16, 1, 512),
     ("f32-std-d64", "f32", 2, 4, 1, 999, 64, 8, 0, 300),
     ("f32-slab", "f32", 1, 4, 4, 1500, 128, 8, 1, 1100),
+    ("bf16-std-d64", "bf16", 2, 4, 2, 2500, 64, 8, 0, 600),
+    ("bf16-slab-d64", "bf16", 2, 4, 1, 1800, 64, 8, 1, 500),
     # B*Hq >= 512: one work-group per selection list (online softmax across its chunks)
     ("bf16-std-onepass", "bf16", 16, 32, 8, 1200, 128, 16, 0, 700),
     ("bf16-slab-onepass", "bf16", 16, 32, 8, 1100, 128, 16, 1, 900),
