@@ -135,6 +135,18 @@ def test_token_topk_standard_layout(sa, case):
     assert np.array_equal(fc.cpu().numpy(), exp)
 
 
+def test_token_topk_slab_d64(sa):
+    """Head dim 64 (32 rotary pairs), 8 dominant pairs: 32-byte slab rows."""
+    say("case: token top-k slab d=64")
+    q, kd, lens_t, dom = _inputs("bf16", 2, 4, 2, 24000, 8, [24000, 17000], 61, d=64)
+    scale = 64 ** -0.5
+    ri, rc = _two_step(sa, q, kd, lens_t, dom, scale, 900)
+    fi, fc = _fused(sa, q, kd, lens_t, dom, scale, 900)
+    torch.cuda.synchronize()
+    assert torch.equal(fc, rc)
+    assert torch.equal(fi, ri)
+
+
 def test_token_topk_pads_wider_output(sa):
     """max_out above k_top: the selection is the same and the rest is -1."""
     q, kd, lens_t, dom = _inputs("bf16", 1, 4, 1, 12000, 16, [11000], 77)
