@@ -489,11 +489,13 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   // clamped to the list width: a count above it never reads past the row
   const int cnt = min(max(((uniform_i32p)blk_cnt)[sel0], 0), max_sel);
   const uniform_i32p sel = (uniform_i32p)(blk_idx + sel0 * max_sel);
+  // the first entry is read beside the count, not after it (one scalar
+  // round trip less before the first tile load)
+  const int J0 = max_sel > 0 ? sel[0] : -1;
+  auto usable = [&](int J) { return J >= 0 && J < N && !(causal && J > I); };
   auto next_valid = [&](int from) {
-    for (int t = from; t < cnt; ++t) {
-      const int J = sel[t];
-      if (J >= 0 && J < N && !(causal && J > I)) return t;
-    }
+    for (int t = from; t < cnt; ++t)
+      if (usable(sel[t])) return t;
     return cnt;
   };
   // chunk cursor: list position t, chunk c within the block (t == cnt: none)
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   st.l_part = 0.f;
 
   // cursors: (t0, c0) = chunk c (scores in sacc), (t1, c1) = chunk c + 1, (t2, c2) = chunk c + 2
-  int t0 = next_valid(0), c0 = 0;
+  int t0 = (cnt > 0 && usable(J0)) ? 0 : next_valid(1), c0 = 0;
   int t1 = t0, c1 = 0;
   advance(t1, c1);
   int t2 = t1, c2 = c1;
@@ -540,12 +542,15 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   for (int r = 0; r < 16; ++r) negm[r] = 0.f;
   f32x16 sacc[2];
   if (t0 < cnt) {
-    // prologue: K(0) -> K0; then K(1) -> K1 and V(0) -> V0 while S(0) is computed
+    // prologue: K(0) -> K0, K(1) -> K1 and V(0) -> V0 issued together; S(0)
+    // waits for Q and K(0) only (the loads complete in order), so K(1) and
+    // V(0) land while it is computed
     Tile::issue(kbase + chunk_row0(t0, c0) * D, sK0, wid, lane);
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
     if (t1 < cnt) Tile::issue(kbase + chunk_row0(t1, c1) * D, sK1, wid, lane);
     Tile::issue(vbase + chunk_row0(t0, c0) * D, sV0, wid, lane);
+    if (t1 < cnt) wait_vmcnt<2 * Tile::LPW>();
+    else wait_vmcnt<Tile::LPW>();
+    __builtin_amdgcn_s_barrier();
     chunk_scores<D>(sK0, off, qf, sacc);
     if (causal && sel[t0] == I) chunk_mask(sacc, c0 * 64, qloc, hi);
     // O and l are still zero: nothing to rescale
