@@ -258,7 +258,9 @@ int sa_prefill_row_params(int N, int64_t heads, int causal, int keep_const, int 
  * sa_sparse_attn_prefill -- block-sparse softmax attention (Prism sec. 1).
  *   q_rope [B, Hq, S, d], k_rope [B, Hkv, S, d], v [B, Hkv, S, d], dtype.
  *   blk_idx [B, Hq, N, max_sel] int32: the key blocks each query block
- *   attends to (ascending, distinct, < N; entries past blk_cnt ignored);
+ *   attends to (ascending, distinct, < N; entries past blk_cnt ignored;
+ *   an entry outside [0, N), or with causal above the diagonal, is skipped
+ *   wherever it sits in the list);
  *   blk_cnt [B, Hq, N] int32 in [0, max_sel] (a count outside that range
  *   is clamped to it on the device, so no read leaves the row).
  *   causal: 1 -> a query at position t sees keys s <= t only (a token mask

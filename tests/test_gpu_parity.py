@@ -529,6 +529,61 @@ def test_prefill_count_above_width_is_clamped(sa, dtype, block):
     assert bool((outs[2][0] == 0).all()) and bool(torch.isneginf(outs[2][1]).all())
 
 
+@pytest.mark.parametrize("dtype,block", [("bf16", 128), ("bf16", 64), ("f32", 64)],
+                         ids=["bf16-b128", "bf16-b64", "f32-plain"])
+def test_prefill_unusable_entries_are_skipped(sa, dtype, block):
+    """List entries outside [0, N) and, with the causal mask, above the
+    diagonal are skipped wherever they sit in the list (first entry
+    included): the output matches the oracle over the usable entries only,
+    and a list of unusable entries alone gives out = 0, lse = -inf."""
+    say(f"case: prefill unusable list entries {dtype} block {block}")
+    B, Hq, Hkv, S, d, max_sel = 1, 4, 1, 1024, 128, 9
+    N = S // block
+    q = _stored((B, Hq, S, d), dtype, 51)
+    k = _stored((B, Hkv, S, d), dtype, 52)
+    v = _stored((B, Hkv, S, d), dtype, 53)
+    g = np.random.default_rng(54)
+    idx = np.full((B, Hq, N, max_sel), -1, np.int32)
+    cnt = np.zeros((B, Hq, N), np.int32)
+    sel = [[[None] * N for _ in range(Hq)]]
+    for h in range(Hq):
+        for I in range(N):
+            good = sorted(set(g.choice(I + 1, size=min(I + 1, 3), replace=False).tolist()) | {I})
+            if h == Hq - 1 and I % 3 == 0:
+                good = []  # only unusable entries
+            bad = [-1, N + 5, -7] + ([I + 1] if I + 1 < N else [N])
+            lst = list(good)
+            for j, x in enumerate(bad):  # the first bad one goes first, the rest in between
+                lst.insert(0 if j == 0 else int(g.integers(0, len(lst) + 1)), x)
+            lst = lst[:max_sel]
+            idx[0, h, I, :len(lst)] = lst
+            cnt[0, h, I] = len(lst)
+            sel[0][h][I] = sorted(x for x in lst if 0 <= x <= I)
+    qd, kd, vd = _dev(q, dtype), _dev(k, dtype), _dev(v, dtype)
+    idx_d, g_idx = guarded(idx.shape, torch.int32)
+    idx_d.copy_(torch.from_numpy(idx))
+    out, g_o = guarded((B, Hq, S, d), _dt(dtype))
+    lse, g_l = guarded((B, Hq, S), torch.float32)
+    scale = d ** -0.5
+    sa.sa_sparse_attn_prefill(qd, kd, vd, idx_d, torch.from_numpy(cnt).to(DEV), out, block=block,
+                              sm_scale=scale, causal=True, lse=lse)
+    torch.cuda.synchronize()
+    check_all(("out", g_o), ("lse", g_l), ("idx", g_idx))
+    ref, rlse = O.prefill_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                    sel, block, scale, True)
+    got = _host(out)
+    err = np.abs(got - ref).max()
+    say(f"  max |out - ref| = {err:.3e}")
+    assert err <= OUT_ATOL[dtype]
+    gl = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.abs(gl[fin] - rlse[fin]).max() <= (1e-4 if dtype == "f32" else LSE_ATOL_BF16)
+    for I in range(0, N, 3):  # the lists of unusable entries alone
+        rows = slice(I * block, (I + 1) * block)
+        assert bool((out[0, Hq - 1, rows] == 0).all()) and bool(torch.isneginf(lse[0, Hq - 1, rows]).all())
+
+
 @pytest.mark.parametrize("B,Hq", [(2, 8), (16, 32)], ids=["split-k", "one-pass"])
 def test_decode_count_above_width_is_clamped(sa, B, Hq):
     """tok_cnt above max_k is clamped on the device to max_k (negative to 0)."""
