@@ -1,7 +1,8 @@
 """A decode step captured once in a HIP graph and replayed: the fused token
 top-k (sa_token_topk) then the decode attention (sa_sparse_attn_decode with
 its workspace, or the allocation-free sa_sparse_attn_decode_static), on the
-standard and the dominant-slab cache layouts.  The library issues only
+standard and the dominant-slab cache layouts; and the prefill layer
+(sa_block_score, sa_topk_select, sa_sparse_attn_prefill) likewise.  The library issues only
 kernel launches on the caller's stream (no memory set, copy, allocation or
 synchronisation), so a serving loop can capture the step and replay it
 with new queries written into the captured query buffer.
@@ -117,4 +118,46 @@ def test_decode_step_graph_replay(sa, case):
         assert torch.equal(g_buf["out"], e_buf["out"]), f"replay {r}: outputs differ"
         assert torch.equal(g_buf["lse"], e_buf["lse"]), f"replay {r}: lse differs"
         say(f"  replay {r}: equal to the eager step")
+    del graph
+
+
+def test_prefill_layer_graph_replay(sa):
+    """The prefill layer (block scores with the fused rotation and pooling,
+    block top-k, block-sparse attention) captured once and replayed with new
+    queries: every replay equals the same layer run eagerly into its own
+    buffers, bit for bit (scores, lists, counts, output, lse)."""
+    from long_context_sparse_apply_amd.pipeline import PrefillLayer
+    say("case: prefill layer in a graph")
+    B, Hq, Hkv, S, d = 1, 8, 2, 4096, 128
+    bf = torch.bfloat16
+
+    def tensor(seed, H):
+        return torch.from_numpy(synth.gaussian_tensor(seed, 8, (B, H, S, d), "bf16")).to(DEV).to(bf)
+
+    q, k, v = tensor(80, Hq), tensor(81, Hkv), tensor(82, Hkv)
+    kw = dict(theta=5e5, block=128, band_split_pair=16, n_sink=1, n_local=2, keep_percent=10)
+    lg, le = PrefillLayer(q, k, v, **kw), PrefillLayer(q, k, v, **kw)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lg.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lg.run()
+    torch.cuda.synchronize()
+    names = ("scores", "blk_idx", "blk_cnt", "out", "lse")
+    for r in range(3):
+        q.copy_(tensor(83 + r, Hq))
+        le.run()
+        torch.cuda.synchronize()
+        for n in names:
+            getattr(lg, n).fill_(-3)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(lg, n), getattr(le, n)), f"replay {r}: {n} differs"
+        say(f"  replay {r}: equal to the eager layer")
     del graph
