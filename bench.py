@@ -540,8 +540,8 @@ def main():
                          "that scales the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only; this build has no multi-GPU path "
-              "(see the sharding design).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(how it would shard is a design note, not code).", file=sys.stderr)
         sys.exit(2)
     import torch
     import long_context_sparse_apply_amd  # noqa: F401  (fails loudly if not built)

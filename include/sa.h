@@ -50,7 +50,7 @@ typedef enum {
   SA_ERR_DTYPE = 3,       /* unknown dtype                                      */
   SA_ERR_RANGE = 4,       /* a parameter outside its documented range           */
   SA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required         */
-  SA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement        */
+  SA_ERR_UNSUPPORTED = 6, /* valid request the library does not implement       */
   SA_ERR_HIP = 7,         /* a HIP launch or runtime call failed                */
   SA_ERR_ACCESS = 8       /* a buffer the device cannot read or write (pageable
                              host memory where pinned memory is allowed)        */
