@@ -292,6 +292,7 @@ PREFILL_CASES = [  # name, dtype, B, Hq, Hkv, S, d, block, max_sel, causal, empt
     ("bf16-d128-b64-noncausal", "bf16", 1, 2, 2, 768, 128, 64, 4, False, False),
     ("bf16-d128-b32-plain", "bf16", 1, 2, 1, 256, 128, 32, 4, True, False),
     ("f32-d128-b128-dense", "f32", 1, 2, 1, 512, 128, 128, 4, True, False),
+    ("bf16-d128-b128-grp8-batch2", "bf16", 2, 8, 1, 2048, 128, 128, 5, True, True),
 ]
 
 
@@ -436,6 +437,8 @@ def test_token_score(sa, case):
 DECODE_CASES = [  # name, dtype, B, Hq, Hkv, L, d, n_dom, slab, max_k
     ("bf16-std", "bf16", 2, 8, 2, 3000, 128, 16, 0, 700),
     ("bf16-slab", "bf16", 2, 8, 2, 2048, 128, 16, 1, 512),
+    ("bf16-std-grp8", "bf16", 2, 16, 2, 2000, 128, 16, 0, 500),
+    ("bf16-slab-grp8", "bf16", 1, 8, 1, 2500, 128, 8, 1, 800),
     ("f32-std-d64", "f32", 2, 4, 1, 999, 64, 8, 0, 300),
     ("f32-slab", "f32", 1, 4, 4, 1500, 128, 8, 1, 1100),
     ("bf16-std-d64", "bf16", 2, 4, 2, 2500, 64, 8, 0, 600),
