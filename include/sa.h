@@ -195,9 +195,10 @@ sa_status sa_token_score(const void* q_rope, const void* k, const void* k_rest, 
  *   SA_ERR_UNSUPPORTED otherwise.
  *   idx_out [B*Hq, max_out] int32 (max_out >= k_top), count_out [B*Hq].
  *   ws: sa_workspace_bytes(SA_OP_TOKEN_TOPK, B*Hq, Lmax, 0, 0, 0) bytes: per
- *   row a sampled threshold, and per row, tile of 4096 tokens and scoring
- *   wave (4 a tile) a candidate count and up to 256 candidates of 8 bytes
- *   (about 8 KiB per row and 4096 tokens).
+ *   row a sampled threshold and the keys of its (up to 4096) samples
+ *   (16 KiB), and per row, tile of 4096 tokens and scoring wave (4 a tile) a
+ *   candidate count and up to 256 candidates of 8 bytes (about 8 KiB per row
+ *   and 4096 tokens).
  *   A row's candidates are the tokens whose scores reach its sampled
  *   threshold; when their number falls outside [k_top, 2*k_top + 1024] (at
  *   most 8192) or a list overflows, the row's selection reads all its tokens

@@ -78,12 +78,13 @@ int token_topk_cap(int k) {
 }
 
 // Workspace of the fused token top-k: thresholds [rows], list counts
-// [rows, tiles, waves] and lists [rows, tiles, waves, kCollectSlots], each
-// part 256-byte aligned.
+// [rows, tiles, waves], lists [rows, tiles, waves, kCollectSlots] and the
+// rows' sample keys [rows, kTokenSampleKeys], each part 256-byte aligned.
 size_t token_topk_ws_bytes(int64_t rows, int Lmax) {
   const size_t tiles = static_cast<size_t>((Lmax + kCollectTile - 1) / kCollectTile);
   const size_t lists = static_cast<size_t>(rows) * tiles * kCollectWaves;
-  return align256(static_cast<size_t>(rows) * 4) + align256(lists * 4) + lists * kCollectSlots * 8;
+  return align256(static_cast<size_t>(rows) * 4) + align256(lists * 4) +
+         align256(lists * kCollectSlots * 8) + static_cast<size_t>(rows) * kTokenSampleKeys * 4;
 }
 
 // Workspace of the offline calibration: full and pair scores, their

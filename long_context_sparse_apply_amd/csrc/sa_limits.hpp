@@ -26,6 +26,8 @@ constexpr int kMaxLongCols = 262144;
 constexpr int kCollectTile = 4096;
 constexpr int kCollectWaves = 4;
 constexpr int kCollectSlots = 256;
+// sample keys a row of the fused token top-k keeps in its workspace
+constexpr int kTokenSampleKeys = 4096;
 
 // fused selection's LDS region: the candidate buffer (cap 64-bit composites)
 // or, on the exact fallback, the row's selection bitmap followed by a buffer

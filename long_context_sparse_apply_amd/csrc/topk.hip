@@ -680,6 +680,11 @@ hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_
 
 constexpr int kSegLenF = 64;                                  // samples a segment (at most)
 constexpr int kSampPerThreadF = kSegs * kSegLenF / kLongThreads;  // 8
+constexpr int kSampCap = kTokenSampleKeys;  // sample keys a row
+static_assert(kSegs * kSegLenF == kSampCap, "a row's samples fill its key slots");
+// With fewer (batch, KV head) groups than this, four work-groups share a
+// group's samples and a pick kernel searches each row's keys
+constexpr int kThrSplitBelow = 256;
 
 
 // The scaled dominant query slice of row `row` in slab channel order, as the
@@ -720,39 +725,57 @@ __device__ __forceinline__ void load_std_row(const T* __restrict__ row, const in
   for (int j = 0; j < NDC; ++j) kv[j] = Elem<T>::load1(row + s_ch[j]);
 }
 
-template <typename T, int NDC, int GRP, bool SLAB>
+// The sampling plan of a row with n cached tokens and budget k: the sample
+// count and the rank whose key becomes the threshold.  Returns false when the
+// row needs no sample (k <= 0 or k >= n: nothing passes; too few samples or a
+// rank past them: every token passes), with the threshold in *fixed.
+__device__ __forceinline__ bool thr_plan(int n, int k, int& seg_len, int& nsamp, int& rank,
+                                         uint32_t& fixed) {
+  if (k <= 0 || k >= n) {
+    fixed = kNoCandidates;
+    return false;
+  }
+  seg_len = n / kSegs < kSegLenF ? n / kSegs : kSegLenF;
+  nsamp = seg_len * kSegs;
+  const double expect = static_cast<double>(k) * nsamp / n;
+  rank = static_cast<int>(expect + 4.0 * sqrt(expect) + 8.0);
+  if (nsamp < 1024 || rank >= nsamp) {
+    fixed = 0u;  // take every token
+    return false;
+  }
+  return true;
+}
+
+// Sampled thresholds of one (batch, KV head) group's query heads.  PARTS ==
+// 1: grid B * Hkv, a work-group scores all the group's samples for every
+// query head and runs each head's radix search itself (thr[row]).  PARTS > 1
+// (few groups: more work-groups to share the sample loads): grid (B * Hkv,
+// PARTS), part p scores rounds [p, p + 1) * KPT / PARTS and stores the keys
+// at keys[row][e] (e = sample index) for token_thr_pick_kernel, which runs
+// the same search over the same keys.  Rows that need no sample get their
+// fixed threshold from the work-group (PARTS == 1) or the pick kernel.
+template <typename T, int NDC, int GRP, bool SLAB, int PARTS>
 __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
     const T* __restrict__ q, const T* __restrict__ kdom, int Hq, int Hkv, int Lmax, int d,
     const int32_t* __restrict__ cache_len, const int32_t* __restrict__ dom, int n_dom, float scale,
-    int k_top, uint32_t* __restrict__ thr) {
+    int k_top, uint32_t* __restrict__ thr, uint32_t* __restrict__ keys) {
   constexpr int R16 = NDC * static_cast<int>(sizeof(T)) / 16;  // 16-byte words a slab row
   static_assert(!SLAB || (R16 >= 1 && R16 <= 8), "slab rows of 16 to 128 bytes");
-  constexpr int KPT = kSampPerThreadF;
-  __shared__ uint32_t s_hist[kBins];
+  static_assert(kSampPerThreadF % PARTS == 0, "rounds split evenly over the parts");
+  constexpr int RPP = kSampPerThreadF / PARTS;  // rounds of this work-group
   __shared__ int s_ch[NDC];
-  __shared__ int s_tmp[kLongThreads / kWave + 4];
   __shared__ __attribute__((aligned(16))) float s_q[GRP][NDC];
-  TopkShared sh{};
-  sh.hist = s_hist;
-  sh.tmp = s_tmp;
-  sh.pick = s_tmp + kLongThreads / kWave;
   const int tid = threadIdx.x;
   const int b = blockIdx.x / Hkv;
   const int g = blockIdx.x % Hkv;
+  const int j0 = PARTS > 1 ? static_cast<int>(blockIdx.y) * RPP : 0;  // first round
   const int64_t row0 = static_cast<int64_t>(b) * Hq + g * GRP;  // the group's first row
   const int n = clamp_len(cache_len[b], Lmax);
-  const int k = k_top;
+  int seg_len = 0, nsamp = 0, rank = 0;
+  uint32_t fixed = 0;
   // uniform over the work-group: all threads return here or none
-  if (k <= 0 || k >= n) {
-    if (tid < GRP) thr[row0 + tid] = kNoCandidates;
-    return;
-  }
-  const int seg_len = n / kSegs < kSegLenF ? n / kSegs : kSegLenF;
-  const int nsamp = seg_len * kSegs;
-  const double expect = static_cast<double>(k) * nsamp / n;
-  const int rank = static_cast<int>(expect + 4.0 * sqrt(expect) + 8.0);
-  if (nsamp < 1024 || rank >= nsamp) {
-    if (tid < GRP) thr[row0 + tid] = 0u;  // take every token
+  if (!thr_plan(n, k_top, seg_len, nsamp, rank, fixed)) {
+    if (PARTS == 1 && tid < GRP) thr[row0 + tid] = fixed;
     return;
   }
 #pragma unroll
@@ -768,12 +791,13 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
   // seg_len its error stays below 1 / seg_len, so the quotient is exact.
   const uint32_t seg_m = 0xFFFFFFFFu / static_cast<uint32_t>(seg_len) + 1u;
   auto seg_of = [&](int e) { return static_cast<int>(__umulhi(static_cast<uint32_t>(e), seg_m)); };
-  // (segment / offset stepped without a division); a sample past nsamp reads
-  // token 0 and its keys are dropped
   const int seg_stride = n / kSegs;
-  const int seg_step = kLongThreads / seg_len, off_step = kLongThreads % seg_len;
-  int seg = tid / seg_len, off = tid % seg_len;
-  uint32_t skey[GRP][KPT];
+  // the token of sample e (a sample past nsamp reads token 0; its key is 0)
+  auto sample_tok = [&](int e) {
+    const int se = seg_of(e);
+    return e < nsamp ? se * seg_stride + (e - se * seg_len) : 0;
+  };
+  uint32_t skey[GRP][RPP];
   if constexpr (SLAB && R16 <= 4) {
     // slab rows of at most 64 bytes: in round j a wave loads its 64 samples'
     // rows with R16 lanes a row (64 / R16 rows an instruction, so each load
@@ -783,15 +807,14 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
     __shared__ uint4 s_rows[kLongThreads / kWave][kWave][R16];
     const int wv = tid / kWave, ln = tid & (kWave - 1);
     const int rsub = ln / R16, part = ln % R16;
-#pragma unroll 1
-    for (int j = 0; j < KPT; ++j) {
+#pragma unroll
+    for (int jj = 0; jj < RPP; ++jj) {
+      const int j = j0 + jj;
       uint4 raw[R16];
 #pragma unroll
       for (int i = 0; i < R16; ++i) {
         const int e = j * kLongThreads + wv * kWave + i * RPI + rsub;  // the sample loaded
-        const int se = seg_of(e);
-        const int tok_e = e < nsamp ? se * seg_stride + (e - se * seg_len) : 0;
-        raw[i] = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(tok_e) * NDC)[part];
+        raw[i] = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(sample_tok(e)) * NDC)[part];
       }
 #pragma unroll
       for (int i = 0; i < R16; ++i) s_rows[wv][i * RPI + rsub][part] = raw[i];
@@ -801,29 +824,26 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
       load_slab_row<T, NDC>(reinterpret_cast<const T*>(&s_rows[wv][ln][0]), kv);
       const bool in = tid + j * kLongThreads < nsamp;
 #pragma unroll
-      for (int hh = 0; hh < GRP; ++hh) skey[hh][j] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
+      for (int hh = 0; hh < GRP; ++hh) skey[hh][jj] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
       __builtin_amdgcn_s_waitcnt(0xC07F);  // the slice's reads done before it is rewritten
       __builtin_amdgcn_wave_barrier();
     }
   } else if constexpr (SLAB) {
-    uint4 w[KPT][R16];
+    uint4 w[RPP][R16];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const bool in = tid + j * kLongThreads < nsamp;
-      const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(in ? seg * seg_stride + off : 0) * NDC);
+    for (int jj = 0; jj < RPP; ++jj) {
+      const uint4* src = reinterpret_cast<const uint4*>(
+          kb + static_cast<int64_t>(sample_tok(tid + (j0 + jj) * kLongThreads)) * NDC);
 #pragma unroll
-      for (int c = 0; c < R16; ++c) w[j][c] = src[c];
-      seg += seg_step;
-      off += off_step;
-      if (off >= seg_len) { off -= seg_len; ++seg; }
+      for (int c = 0; c < R16; ++c) w[jj][c] = src[c];
     }
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
+    for (int jj = 0; jj < RPP; ++jj) {
       float kv[NDC];
-      load_slab_row<T, NDC>(reinterpret_cast<const T*>(&w[j][0]), kv);
-      const bool in = tid + j * kLongThreads < nsamp;
+      load_slab_row<T, NDC>(reinterpret_cast<const T*>(&w[jj][0]), kv);
+      const bool in = tid + (j0 + jj) * kLongThreads < nsamp;
 #pragma unroll
-      for (int hh = 0; hh < GRP; ++hh) skey[hh][j] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
+      for (int hh = 0; hh < GRP; ++hh) skey[hh][jj] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
     }
   } else if constexpr (sizeof(T) == 2 && NDC <= 32) {
     // standard rows, bf16, up to 32 scored channels: in round j a wave loads
@@ -836,15 +856,14 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
     const int wv = tid / kWave, ln = tid & (kWave - 1);
     const int rsub = ln / NDC, slot = ln % NDC;
     const int ch = s_ch[slot];
-#pragma unroll 1
-    for (int j = 0; j < KPT; ++j) {
+#pragma unroll
+    for (int jj = 0; jj < RPP; ++jj) {
+      const int j = j0 + jj;
       uint16_t raw[kWave / RPI];
 #pragma unroll
       for (int i = 0; i < kWave / RPI; ++i) {
         const int e = j * kLongThreads + wv * kWave + i * RPI + rsub;  // the sample loaded
-        const int se = seg_of(e);
-        const int tok_e = e < nsamp ? se * seg_stride + (e - se * seg_len) : 0;
-        raw[i] = reinterpret_cast<const uint16_t*>(kb)[static_cast<int64_t>(tok_e) * d + ch];
+        raw[i] = reinterpret_cast<const uint16_t*>(kb)[static_cast<int64_t>(sample_tok(e)) * d + ch];
       }
 #pragma unroll
       for (int i = 0; i < kWave / RPI; ++i) s_raw[wv][i * RPI + rsub][slot] = raw[i];
@@ -855,41 +874,82 @@ __global__ __launch_bounds__(kLongThreads) void token_thr_kernel(
       for (int c = 0; c < NDC; ++c) kv[c] = __uint_as_float(static_cast<uint32_t>(s_raw[wv][ln][c]) << 16);
       const bool in = tid + j * kLongThreads < nsamp;
 #pragma unroll
-      for (int hh = 0; hh < GRP; ++hh) skey[hh][j] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
+      for (int hh = 0; hh < GRP; ++hh) skey[hh][jj] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv)) : 0u;
       __builtin_amdgcn_s_waitcnt(0xC07F);  // the slice's reads done before it is rewritten
       __builtin_amdgcn_wave_barrier();
     }
   } else {
     // standard rows: the scored channels of RND samples at a time
-    int tok[KPT];
+    int tok[RPP];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      tok[j] = tid + j * kLongThreads < nsamp ? seg * seg_stride + off : 0;
-      seg += seg_step;
-      off += off_step;
-      if (off >= seg_len) { off -= seg_len; ++seg; }
-    }
-    constexpr int RND = NDC >= 64 ? 1 : (64 / NDC < KPT ? 64 / NDC : KPT);
+    for (int jj = 0; jj < RPP; ++jj) tok[jj] = sample_tok(tid + (j0 + jj) * kLongThreads);
+    constexpr int RND = NDC >= 64 ? 1 : (64 / NDC < RPP ? 64 / NDC : RPP);
 #pragma unroll
-    for (int j0 = 0; j0 < KPT; j0 += RND) {
+    for (int r0 = 0; r0 < RPP; r0 += RND) {
       float kv[RND][NDC];
 #pragma unroll
       for (int jj = 0; jj < RND; ++jj)
-        load_std_row<T, NDC>(kb + static_cast<int64_t>(tok[j0 + jj]) * d, s_ch, kv[jj]);
+        load_std_row<T, NDC>(kb + static_cast<int64_t>(tok[r0 + jj]) * d, s_ch, kv[jj]);
 #pragma unroll
       for (int jj = 0; jj < RND; ++jj) {
-        const bool in = tid + (j0 + jj) * kLongThreads < nsamp;
+        const bool in = tid + (j0 + r0 + jj) * kLongThreads < nsamp;
 #pragma unroll
         for (int hh = 0; hh < GRP; ++hh)
-          skey[hh][j0 + jj] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv[jj])) : 0u;
+          skey[hh][r0 + jj] = in ? order_key(token_dot<NDC>(&s_q[hh][0], kv[jj])) : 0u;
       }
     }
   }
+  if constexpr (PARTS == 1) {
+    __shared__ uint32_t s_hist[kBins];
+    __shared__ int s_tmp[kLongThreads / kWave + 4];
+    TopkShared sh{};
+    sh.hist = s_hist;
+    sh.tmp = s_tmp;
+    sh.pick = s_tmp + kLongThreads / kWave;
 #pragma unroll
-  for (int hh = 0; hh < GRP; ++hh) {
-    const uint32_t t_low = sampled_threshold_t<KPT>(sh, skey[hh], nsamp, rank);
-    if (tid == 0) thr[row0 + hh] = t_low;
+    for (int hh = 0; hh < GRP; ++hh) {
+      const uint32_t t_low = sampled_threshold_t<RPP>(sh, skey[hh], nsamp, rank);
+      if (tid == 0) thr[row0 + hh] = t_low;
+    }
+  } else {
+    // sample e = tid + j kLongThreads of row row0 + hh at keys[(row0 + hh) kSampCap + e]
+#pragma unroll
+    for (int hh = 0; hh < GRP; ++hh)
+#pragma unroll
+      for (int jj = 0; jj < RPP; ++jj)
+        keys[(row0 + hh) * kSampCap + tid + (j0 + jj) * kLongThreads] = skey[hh][jj];
   }
+}
+
+// The sampled threshold of each (batch, query head) row from its sample keys
+// (one work-group a row): the same radix search over the same keys, in the
+// same per-thread layout, as when one work-group scored and selected a
+// group's samples itself.
+__global__ __launch_bounds__(kLongThreads) void token_thr_pick_kernel(
+    int Hq, int Lmax, const int32_t* __restrict__ cache_len, int k_top,
+    const uint32_t* __restrict__ keys, uint32_t* __restrict__ thr) {
+  constexpr int KPT = kSampPerThreadF;
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ int s_tmp[kLongThreads / kWave + 4];
+  TopkShared sh{};
+  sh.hist = s_hist;
+  sh.tmp = s_tmp;
+  sh.pick = s_tmp + kLongThreads / kWave;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int b = static_cast<int>(row / Hq);
+  const int n = clamp_len(cache_len[b], Lmax);
+  int seg_len = 0, nsamp = 0, rank = 0;
+  uint32_t fixed = 0;
+  if (!thr_plan(n, k_top, seg_len, nsamp, rank, fixed)) {
+    if (tid == 0) thr[row] = fixed;
+    return;
+  }
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = keys[row * kSampCap + tid + j * kLongThreads];
+  const uint32_t t_low = sampled_threshold_t<KPT>(sh, key, nsamp, rank);
+  if (tid == 0) thr[row] = t_low;
 }
 
 template <typename T, int NDC, bool SLAB>
@@ -1026,8 +1086,8 @@ __global__ __launch_bounds__(kLongThreads) void token_select_kernel(
 }
 
 // Workspace (sized by token_topk_ws_bytes): thresholds [rows], list counts
-// [rows, tiles, waves] and lists [rows, tiles, waves, kCollectSlots], each
-// part 256-byte aligned.
+// [rows, tiles, waves], lists [rows, tiles, waves, kCollectSlots] and sample
+// keys [rows, kSampCap], each part 256-byte aligned.
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int Hq, int Hkv,
@@ -1043,7 +1103,10 @@ hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int
   uint32_t* thr = reinterpret_cast<uint32_t*>(w);
   int* cnt = reinterpret_cast<int*>(w + align256(static_cast<size_t>(rows) * 4));
   uint64_t* cand = reinterpret_cast<uint64_t*>(w + align256(static_cast<size_t>(rows) * 4) + align256(lists * 4));
+  uint32_t* skeys = reinterpret_cast<uint32_t*>(w + align256(static_cast<size_t>(rows) * 4) + align256(lists * 4) +
+                                                align256(lists * kCollectSlots * 8));
   const TokenCollect col{thr, cnt, cand, tiles};
+  const bool split = static_cast<int64_t>(B) * Hkv < kThrSplitBelow;
   const size_t lds = token_select_lds_bytes(Lmax, cap);
   // scored slots: exactly 2 n_dom in the slab, a power of two of at least 8
   // covering them in the standard layout (as the scoring kernel has it)
@@ -1051,8 +1114,13 @@ hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int
   const int ndc = slab ? need : (need <= 8 ? 8 : need <= 16 ? 16 : need <= 32 ? 32 : need <= 64 ? 64 : 128);
   const int grp = Hq / Hkv;
 #define SA_TT_G(T, C, SL, G)                                                                        \
-  token_thr_kernel<T, C, G, SL><<<dim3(static_cast<unsigned>(B * Hkv)), kLongThreads, 0, st>>>(    \
-      qq, kk, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, scale, k_top, thr)
+  if (split)                                                                                        \
+    token_thr_kernel<T, C, G, SL, 4><<<dim3(static_cast<unsigned>(B * Hkv), 4), kLongThreads, 0,   \
+                                       st>>>(qq, kk, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, scale,  \
+                                             k_top, thr, skeys);                                     \
+  else                                                                                              \
+    token_thr_kernel<T, C, G, SL, 1><<<dim3(static_cast<unsigned>(B * Hkv)), kLongThreads, 0, st>>>( \
+        qq, kk, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, scale, k_top, thr, skeys)
 #define SA_TT(T, C, SL)                                                                             \
   do {                                                                                              \
     const auto* qq = static_cast<const T*>(q);                                                      \
@@ -1070,6 +1138,12 @@ hipError_t launch_token_topk(const void* q, const void* k, int dtype, int B, int
     }                                                                                               \
     e = hipGetLastError();                                                                          \
     if (e != hipSuccess) return e;                                                                  \
+    if (split) {                                                                                    \
+      token_thr_pick_kernel<<<dim3(static_cast<unsigned>(rows)), kLongThreads, 0, st>>>(            \
+          Hq, Lmax, cache_len, k_top, skeys, thr);                                                  \
+      e = hipGetLastError();                                                                        \
+      if (e != hipSuccess) return e;                                                                \
+    }                                                                                               \
     e = launch_token_collect(q, k, dtype, B, Hq, Hkv, Lmax, d, cache_len, dom, n_dom, slab, scale,  \
                              col, st);                                                              \
     if (e != hipSuccess) return e;                                                                  \

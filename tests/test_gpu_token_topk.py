@@ -83,6 +83,9 @@ CASES = [  # name, dtype, B, Hq, Hkv, Lmax, n_dom, lens, k_top, tie
     ("f32-sampled", "f32", 2, 4, 2, 20000, 8, [20000, 15000], 700, False),
     ("f32-narrow", "f32", 1, 2, 2, 6000, 4, [6000], 100, False),
     ("bf16-all-tied-fallback", "bf16", 1, 4, 1, 16384, 16, [16384], 512, True),
+    # 256 (batch, KV head) groups: one work-group samples and searches a group
+    # (fewer groups: four work-groups share the samples, a pick kernel searches)
+    ("bf16-256-groups", "bf16", 64, 8, 4, 8192, 16, [8192 - 37 * i for i in range(64)], 512, False),
 ]
 
 
@@ -114,6 +117,8 @@ STD_CASES = [  # name, dtype, d, B, Hq, Hkv, Lmax, n_dom, lens, k_top, tie
     ("std-f32", "f32", 128, 2, 4, 2, 20000, 16, [20000, 15000], 700, False),
     ("std-bf16-k-above-len", "bf16", 128, 2, 4, 2, 3000, 16, [3000, 2500], 2800, False),
     ("std-bf16-all-tied-fallback", "bf16", 128, 1, 4, 1, 16384, 16, [16384], 512, True),
+    ("std-bf16-256-groups", "bf16", 128, 64, 8, 4, 8192, 16, [8192 - 37 * i for i in range(64)], 512,
+     False),
 ]
 
 
