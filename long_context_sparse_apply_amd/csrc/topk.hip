@@ -665,6 +665,8 @@ hipError_t launch_topk(const float* scores, int64_t rows, int cols, const int32_
 //     kSegs x kSegLenF sampled tokens (each sample's row read once for all
 //     heads).  Rows with k = 0 or k >= their length get a threshold
 //     nothing passes, rows too short to sample one that takes every token.
+//     With few groups, four work-groups share a group's samples and
+//     token_thr_pick_kernel finishes each row's threshold from their keys.
 //  2. the token scoring kernel in collect mode (token_score.hip): the same
 //     scores as the scoring entry point; tokens at or above the threshold go
 //     to per-wave candidate lists (no atomics).
