@@ -49,7 +49,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const int sub = lane % LPT;
   const int grp_tok = lane / LPT;
   const int split = blockIdx.x;
-  const int bh = blockIdx.y;
+  // one pass over a multiple of 8 lists: list ids in XCD-contiguous ranges
+  // (work-groups go to the 8 XCDs in turn), so the query heads of a KV group
+  // share an XCD and a row that two of them select can come from its L2
+  int bh = blockIdx.y;
+  if (gridDim.x == 1 && (gridDim.y & 7) == 0) bh = (bh & 7) * (gridDim.y >> 3) + (bh >> 3);
   const int h = bh % Hq;
   const int b = bh / Hq;
   const int g = h / (Hq / Hkv);
