@@ -72,7 +72,15 @@ __global__ __launch_bounds__(256) void block_gemm_mfma_kernel(const float* __res
                                                               int Hkv, int N, float scale,
                                                               int causal,
                                                               float* __restrict__ scores) {
-  const int ti = blockIdx.x, tj = blockIdx.y, bh = blockIdx.z;
+  // the tiles of a head in one XCD-contiguous range of work-group ids
+  // (work-groups go to the 8 XCDs in turn), so the head's pooled rows are
+  // fetched into one L2, not eight
+  const int64_t gx = gridDim.x, gy = gridDim.y;
+  const int64_t nwg = gx * gy * gridDim.z;
+  int64_t wl = (blockIdx.z * gy + blockIdx.y) * gx + blockIdx.x;
+  if ((nwg & 7) == 0) wl = (wl & 7) * (nwg >> 3) + (wl >> 3);
+  const int ti = static_cast<int>(wl % gx), tj = static_cast<int>((wl / gx) % gy);
+  const int bh = static_cast<int>(wl / (gx * gy));
   const int h = bh % Hq, b = bh / Hq, g = h / (Hq / Hkv);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
