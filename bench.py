@@ -334,6 +334,30 @@ def copy_reference(torch, reps=5):
     return 2.0 * (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9
 
 
+def gemm_reference(torch, n=8192, per_group=25, groups=3):
+    """Achieved TFLOP/s of a plain bf16 matrix product (n x n times n x n,
+    contiguous operands, torch.matmul on the vendor GEMM library), timed in
+    the same run as a practical matrix-unit reference: `per_group` products
+    back to back between two events, so the chip settles at the clock it
+    sustains under matrix load; the median over `groups` groups."""
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(groups):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(per_group):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / per_group)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return 2.0 * n ** 3 / (float(np.median(ts)) * 1e-3) / 1e12
+
+
 def run_prefill(cfg, steps, warmup, torch, flush):
     import synth.device as SD
     from long_context_sparse_apply_amd.pipeline import PrefillLayer
@@ -532,7 +556,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default=None, help="C2|C3|C4|C5: run one workload (profiling)")
+    ap.add_argument("--only", default=None, help="C2|C3|C4|C4_SLAB|C5: run one workload (profiling)")
     ap.add_argument("--no-flush", action="store_true",
                     help="do not clear L2 / MALL with a 1 GiB read sweep before each timed step")
     ap.add_argument("--calib-copy", action="store_true",
@@ -568,6 +592,8 @@ def main():
 
     copy_gbps = copy_reference(torch)
     log(f"1 GiB device copy: {copy_gbps:.0f} GB/s")
+    gemm_tflops = gemm_reference(torch)
+    log(f"bf16 8192^3 library matrix product: {gemm_tflops:.0f} TFLOP/s")
     cfg = W.C2
     log("C2: prefill 32K")
     main_r = run_prefill(cfg, args.steps, args.warmup, torch, flush)
@@ -582,7 +608,8 @@ def main():
                                      "attend_ms": r3["attend_ms"],
                                      "attend_mfma_frac": r3["attend_mfma_frac"],
                                      "score_ms": r3["score_ms"], "select_ms": r3["select_ms"]}
-        for name, c in (("decode_64k", W.C4), ("decode_128k_slab", W.C5),
+        for name, c in (("decode_64k", W.C4), ("decode_64k_slab", W.C4_SLAB),
+                        ("decode_128k_slab", W.C5),
                         ("decode_128k_slab_rest", W.C5.with_(full_rows=0))):
             log(f"{name}")
             rd = run_decode(c, args.steps, args.warmup, torch, flush)
@@ -676,6 +703,9 @@ def main():
                    "cleared by a 1 GiB read sweep before each step" if not args.no_flush else
                    "HIP events on the kernels' stream; medians of the timed steps; no cache flush"),
         "hbm_reference": {"copy_GBps": copy_gbps, "peak_GBps": PEAK_HBM_BPS / 1e9},
+        "mfma_reference": {"gemm_TFLOPs": gemm_tflops, "peak_TFLOPs": PEAK_BF16_FLOPS / 1e12,
+                           "gemm": "bf16 8192 x 8192 x 8192, torch.matmul (vendor library)",
+                           "attend_vs_gemm": main_r["attend_tflops"] / gemm_tflops},
         "cpu_baseline": cpu,
         "cpu_baseline_secondary": cpu_more,
         "secondary": secondary,

@@ -108,7 +108,12 @@ C5 = DecodeConfig("token-sparse decode, batch 64, KV length 131072, dominant sla
                   "bf16", 64, 32, 8, 131072, 128, 5e5, n_dom=16, k=4096, slab=1, seed=5,
                   full_rows=1)
 
-CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
+# the 64K decode workload with the 128K workload's cache layout: the same logical
+# K cache (same seed and channels) as C4, stored as the dominant slab plus full rows
+C4_SLAB = C4.with_(name="token-sparse decode, batch 16, KV length 65536, dominant slab + full rows, "
+                        "bf16", slab=1, full_rows=1)
+
+CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C4_SLAB": C4_SLAB}
 
 
 # ---------------------------------------------------------------- rotation used to plant

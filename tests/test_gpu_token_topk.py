@@ -197,3 +197,29 @@ def test_token_topk_decode_c4_shape(sa):
     torch.cuda.synchronize()
     assert torch.equal(fused.tok_cnt, rc)
     assert torch.equal(fused.tok_idx, ri)
+
+
+def test_decode_c4_slab_layout_matches_standard(sa):
+    """The 64K decode workload (batch 16, top-2048) on the dominant slab +
+    full-row cache: the slab holds the dominant channels in the order the
+    standard layout scores them, and the full rows equal the standard cache,
+    so the step selects the same tokens and attends to the same output, bit
+    for bit, as on the standard cache."""
+    from long_context_sparse_apply_amd.pipeline import DecodeStep
+    import synth.device as SD
+    res = []
+    for cfg in (W.C4, W.C4_SLAB):
+        dt = SD.decode_tensors(cfg)
+        step = DecodeStep(dt["q_raw"], dt["k"], dt["v"], dt["lens"], dt["dom"], theta=cfg.theta,
+                          top_k=cfg.k, slab=bool(cfg.slab), k_rest=dt["k_rest"],
+                          k_full=dt["k_full"])
+        assert step.fused
+        step.run()
+        torch.cuda.synchronize()
+        res.append((step.tok_idx.clone(), step.tok_cnt.clone(), step.out.clone()))
+        del step, dt
+        torch.cuda.empty_cache()
+    (i0, c0, o0), (i1, c1, o1) = res
+    assert torch.equal(c0, c1)
+    assert torch.equal(i0, i1)
+    assert torch.equal(o0, o1)
