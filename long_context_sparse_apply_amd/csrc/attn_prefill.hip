@@ -493,17 +493,26 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   // round trip less before the first tile load)
   const int J0 = max_sel > 0 ? sel[0] : -1;
   auto usable = [&](int J) { return J >= 0 && J < N && !(causal && J > I); };
-  auto next_valid = [&](int from) {
-    for (int t = from; t < cnt; ++t)
-      if (usable(sel[t])) return t;
+  // the first usable entry at or after `from` (cnt: none), its block in jj
+  auto next_valid = [&](int from, int& jj) {
+    for (int t = from; t < cnt; ++t) {
+      const int j = sel[t];
+      if (usable(j)) {
+        jj = j;
+        return t;
+      }
+    }
+    jj = -1;
     return cnt;
   };
   // chunk cursor: list position t, chunk c within the block (t == cnt: none)
-  auto advance = [&](int& tt, int& cc) {
+  // and the block's index jj, read from the list once per block, so a step
+  // issues its tile loads without waiting for a scalar load of the list
+  auto advance = [&](int& tt, int& cc, int& jj) {
     if (tt >= cnt) return;
-    if (cc + 1 < CPB) { ++cc; } else { tt = next_valid(tt + 1); cc = 0; }
+    if (cc + 1 < CPB) { ++cc; } else { tt = next_valid(tt + 1, jj); cc = 0; }
   };
-  auto chunk_row0 = [&](int tt, int cc) { return static_cast<int64_t>(sel[tt]) * BS + cc * 64; };
+  auto chunk_row0 = [&](int jj, int cc) { return static_cast<int64_t>(jj) * BS + cc * 64; };
 
   // Q^T fragments: this lane's query and 8 channels per k-step
   const int qloc = wid * 32 + l32;
@@ -529,11 +538,12 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   st.l_part = 0.f;
 
   // cursors: (t0, c0) = chunk c (scores in sacc), (t1, c1) = chunk c + 1, (t2, c2) = chunk c + 2
-  int t0 = (cnt > 0 && usable(J0)) ? 0 : next_valid(1), c0 = 0;
-  int t1 = t0, c1 = 0;
-  advance(t1, c1);
-  int t2 = t1, c2 = c1;
-  advance(t2, c2);
+  int j0 = J0;
+  int t0 = (cnt > 0 && usable(J0)) ? 0 : next_valid(1, j0), c0 = 0;
+  int t1 = t0, c1 = 0, j1 = j0;
+  advance(t1, c1, j1);
+  int t2 = t1, c2 = c1, j2 = j1;
+  advance(t2, c2, j2);
 
   ChunkOffsets<D> off;
   off.init(l32, hi, grp16, i16);
@@ -545,14 +555,14 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     // prologue: K(0) -> K0, K(1) -> K1 and V(0) -> V0 issued together; S(0)
     // waits for Q and K(0) only (the loads complete in order), so K(1) and
     // V(0) land while it is computed
-    Tile::issue(kbase + chunk_row0(t0, c0) * D, sK0, wid, lane);
-    if (t1 < cnt) Tile::issue(kbase + chunk_row0(t1, c1) * D, sK1, wid, lane);
-    Tile::issue(vbase + chunk_row0(t0, c0) * D, sV0, wid, lane);
+    Tile::issue(kbase + chunk_row0(j0, c0) * D, sK0, wid, lane);
+    if (t1 < cnt) Tile::issue(kbase + chunk_row0(j1, c1) * D, sK1, wid, lane);
+    Tile::issue(vbase + chunk_row0(j0, c0) * D, sV0, wid, lane);
     if (t1 < cnt) wait_vmcnt<2 * Tile::LPW>();
     else wait_vmcnt<Tile::LPW>();
     __builtin_amdgcn_s_barrier();
     chunk_scores<D>(sK0, off, qf, sacc);
-    if (causal && sel[t0] == I) chunk_mask(sacc, c0 * 64, qloc, hi);
+    if (causal && j0 == I) chunk_mask(sacc, c0 * 64, qloc, hi);
     // O and l are still zero: nothing to rescale
     st.m_ref = chunk_maxval(sacc, sl2);
     if (UNIT) {
@@ -573,13 +583,13 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   auto step = [&](const uint8_t* kread, uint8_t* kwrite, const uint8_t* vread, uint8_t* vwrite) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (t2 < cnt) Tile::issue(kbase + chunk_row0(t2, c2) * D, kwrite, wid, lane);
-    if (t1 < cnt) Tile::issue(vbase + chunk_row0(t1, c1) * D, vwrite, wid, lane);
+    if (t2 < cnt) Tile::issue(kbase + chunk_row0(j2, c2) * D, kwrite, wid, lane);
+    if (t1 < cnt) Tile::issue(vbase + chunk_row0(j1, c1) * D, vwrite, wid, lane);
     off.pin();
     const bool next = t1 < cnt;
     f32x16 snext[2];
     float mblk = chunk_step<D, UNIT>(kread, vread, off, qf, sacc, snext, st, sl2, negm);
-    if (causal && next && sel[t1] == I) {  // uniform: chunk c + 1 is on the diagonal
+    if (causal && next && j1 == I) {  // uniform: chunk c + 1 is on the diagonal
       chunk_mask(snext, c1 * 64, qloc, hi);
       mblk = chunk_maxval(snext, sl2);
     }
@@ -588,8 +598,8 @@ __global__ __launch_bounds__(BS * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) sacc[kt] = snext[kt];
     t0 = t1; c0 = c1;
-    t1 = t2; c1 = c2;
-    advance(t2, c2);
+    t1 = t2; c1 = c2; j1 = j2;
+    advance(t2, c2, j2);
   };
   while (t0 < cnt) {
     step(sK1, sK0, sV0, sV1);  // c even: K(c+1) in K1, V(c) in V0
