@@ -49,7 +49,10 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
                                                         int n_sink, int n_local, int32_t* __restrict__ idx_out,
                                                         int max_out, int32_t* __restrict__ count_out) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  // the wave's row, in a scalar register: the row's length, k and the
+  // search's threshold are then scalars and the search a uniform loop
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wv;
   if (row >= rows) return;
   int n, k;
   row_params(row, cols, valid_len, k_per_row, k_const, n, k);
@@ -88,18 +91,20 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
     // T: the largest key with at least k candidates at or above it, bit by
     // bit from the top.  Once exactly k are at or above T the k best are
     // known (they are the keys >= T) and the lower bits cannot change the
-    // selection, so the search stops there.
+    // selection, so the search stops there.  The tests need no candidate
+    // mask: every tested t is at least 1, a candidate's key at least
+    // 0x007fffff, and every other slot's key 0.
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t t = T | (1u << bit);
       int cnt = 0;
 #pragma unroll
-      for (int j = 0; j < E; ++j) cnt += __popcll(__ballot(((candm >> j) & 1u) && key[j] >= t));
+      for (int j = 0; j < E; ++j) cnt += __popcll(__ballot(key[j] >= t));
       if (cnt >= k) T = t;
       if (cnt == k) break;
     }
     int gt = 0;
 #pragma unroll
-    for (int j = 0; j < E; ++j) gt += __popcll(__ballot(((candm >> j) & 1u) && key[j] > T));
+    for (int j = 0; j < E; ++j) gt += __popcll(__ballot(key[j] > T));
     need = k - gt;
   }
   // k >= ncand: T = 0 and every candidate key is > 0, so all are kept
