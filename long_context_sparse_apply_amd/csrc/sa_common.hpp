@@ -119,6 +119,13 @@ __device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, int voff
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, voffset, 0, 0, 0);
 }
+// The same with the nontemporal hint (cache-policy bit 1, `nt`), for data a
+// kernel streams through once: its lines are the first the L2 gives up.
+__device__ __forceinline__ void lds_dma16_buf_nt(__amdgpu_buffer_rsrc_t r, int voffset,
+                                                 void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, voffset, 0, 0, 2);
+}
 
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float wave_max(float v) {
