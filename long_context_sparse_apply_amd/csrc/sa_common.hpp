@@ -37,6 +37,14 @@ template <> struct Elem<float> {
   static __device__ __forceinline__ Raw load_raw8(const float* p) {
     return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
+  // the same with the nontemporal hint (data read once: its lines are the
+  // first the L2 gives up)
+  static __device__ __forceinline__ Raw load_raw8_nt(const float* p) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f a = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    const v4f b = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + 4));
+    return Raw{make_float4(a.x, a.y, a.z, a.w), make_float4(b.x, b.y, b.z, b.w)};
+  }
   static __device__ __forceinline__ Raw zero_raw8() {
     return Raw{make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
   }
@@ -61,6 +69,11 @@ template <> struct Elem<uint16_t> {
   using Raw = uint4;
   static __device__ __forceinline__ Raw load_raw8(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
+  }
+  static __device__ __forceinline__ Raw load_raw8_nt(const uint16_t* p) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
   }
   static __device__ __forceinline__ Raw zero_raw8() { return make_uint4(0u, 0u, 0u, 0u); }
   static __device__ __forceinline__ void unpack8(const Raw& a, float* v) {
@@ -101,6 +114,10 @@ __device__ __forceinline__ void rot_cos_sin(int64_t p, double f, float& c, float
 // compilation of the calling kernels never sees the builtin.
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+// the same with the nontemporal hint (cache-policy bit 1, `nt`)
+__device__ __forceinline__ void lds_dma16_nt(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 2);
 }
 
 // The same through a buffer resource (buffer_load_dwordx4 ... lds): lane i

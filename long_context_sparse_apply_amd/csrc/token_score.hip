@@ -115,11 +115,11 @@ __global__ __launch_bounds__(256) void token_score_kernel(
   // stage chunk c's rows (tokens past the cache end re-read its last row);
   // the collect instances load through a buffer resource over this (b, KV
   // head)'s rows (at most 64 MiB), whose LDS writes the compiler tracks per
-  // buffer, with the nontemporal hint: every key row is read once, and the
-  // candidate lists written between the reads are small partial lines.
-  // With the hint the pass reads at 5.9-6.2 TB/s instead of 5.2 (kernel
-  // traces: standard rows at 64K 413 -> 344 us, the 128K slab 826 -> 730 us,
-  // the same selections)
+  // buffer.  Both forms load with the nontemporal hint: every key row is read
+  // once, and the candidate lists written between the reads are small
+  // partial lines.  With the hint the collect pass reads at 5.9-6.2 TB/s
+  // instead of 5.2 (kernel traces: standard rows at 64K 413 -> 344 us, the
+  // 128K slab 826 -> 730 us, the same selections)
   const auto rsrc = buffer_rsrc(kb, Lmax * ROWB);
   auto issue_one = [&](int c, int j, uint8_t* buf) {
     const int ins = wid * LPW + j;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void token_score_kernel(
     if constexpr (COLLECT)
       lds_dma16_buf_nt(rsrc, byte, buf + ins * 1024);
     else
-      lds_dma16(kb + byte, buf + ins * 1024);
+      lds_dma16_nt(kb + byte, buf + ins * 1024);
   };
   auto issue = [&](int c, uint8_t* buf) {
 #pragma unroll

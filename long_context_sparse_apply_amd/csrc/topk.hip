@@ -549,7 +549,10 @@ __global__ __launch_bounds__(kLongThreads) void topk_block_kernel(
 #pragma unroll
         for (int u = 0; u < kCollectVec; ++u) {
           const int i = bbase + (u * kLongThreads + tid) * 4;
-          dst[u] = *reinterpret_cast<const float4*>(s + (i < a1 ? i : a0));
+          // (nontemporal: the row is streamed once)
+          typedef float v4f __attribute__((ext_vector_type(4)));
+          const v4f t4 = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(s + (i < a1 ? i : a0)));
+          dst[u] = make_float4(t4.x, t4.y, t4.z, t4.w);
         }
       };
       // the wave's qualifying values of a batch take one LDS atomic for their
