@@ -1083,12 +1083,31 @@ __global__ __launch_bounds__(kLongThreads) void token_select_kernel(
   const int rowlen = SLAB ? NDC : d;
   const T* kb = kdom + (static_cast<int64_t>(b) * Hkv + g) * Lmax * rowlen;
   auto val = [&](int i) {
-    float kv[NDC];
-    if constexpr (SLAB)
+    if constexpr (SLAB) {
+      float kv[NDC];
       load_slab_row<T, NDC>(kb + static_cast<int64_t>(i) * NDC, kv);
-    else
-      load_std_row<T, NDC>(kb + static_cast<int64_t>(i) * d, s_ch, kv);
-    return token_dot<NDC>(s_q, kv);
+      return token_dot<NDC>(s_q, kv);
+    } else {
+      // token_dot's chain (one fused multiply-add a channel, in slot order,
+      // from zero) four channels at a time: the same score bit for bit, with
+      // four scattered loads live instead of NDC, so this rare path does not
+      // set the register count of the whole kernel
+      const T* rowp = kb + static_cast<int64_t>(i) * d;
+      float acc = 0.f;
+#pragma unroll 1
+      for (int j = 0; j < NDC; j += 4) {
+        const float4 qv = *reinterpret_cast<const float4*>(s_q + j);
+        const float k0 = Elem<T>::load1(rowp + s_ch[j]);
+        const float k1 = Elem<T>::load1(rowp + s_ch[j + 1]);
+        const float k2 = Elem<T>::load1(rowp + s_ch[j + 2]);
+        const float k3 = Elem<T>::load1(rowp + s_ch[j + 3]);
+        acc = fmaf(qv.x, k0, acc);
+        acc = fmaf(qv.y, k1, acc);
+        acc = fmaf(qv.z, k2, acc);
+        acc = fmaf(qv.w, k3, acc);
+      }
+      return acc;
+    }
   };
   select_from_source(sh, val, 0, n, k);
   __syncthreads();
