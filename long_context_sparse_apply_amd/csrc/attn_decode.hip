@@ -133,8 +133,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
       tok[it] = (t >= 0 && t < Lmax) ? t : -1;  // out-of-range entries are ignored
     }
     // gather every key and value row of the wave before using any of them,
-    // with the nontemporal hint (the C4 / C5 attentions 98-101 -> 92-93 us and
-    // 703-707 -> 655-656 us with it, outputs unchanged)
+    // with the nontemporal hint (the decode attention at batch 16 / 64K cache
+    // 98-101 -> 92-93 us and at batch 64 / 128K 703-707 -> 655-656 us with
+    // it, outputs unchanged)
     Raw kr[STEPS], vr[STEPS];
 #pragma unroll
     for (int it = 0; it < STEPS; ++it) {
